@@ -1,0 +1,230 @@
+"""Python face of the CPU oracle (``fp4_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY.  Imported by ``tests/``, by ``__graft_entry__.smoke``
+and by the CPU-baseline leg of ``bench.py``; never by the library.  It shares
+no code with the HIP path.
+
+Every function takes and returns numpy arrays.  Layouts (row-major):
+  x           float32 [rows][ld_x]
+  q           uint8   [rows][k/2]   element 2i in the low nibble of byte i
+  sf          uint8   [rows][k/16]  E4M3 block scales
+  w_q         uint8   [E][n][k/2]
+  w_sf        uint8   [E][n][k/16]
+  w_scale     float32 [E]
+  offsets     int32   [E+1]         rows of expert e are [offsets[e], offsets[e+1])
+  a_row_index int32   [m_total] or None (identity)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fp4_oracle.c")
+LIB_PATH = os.environ.get("FP4_ORACLE_LIB") or os.path.join(_HERE, "liboracle_fp4.so")
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no FP contraction).
+
+    FP4_ORACLE_LIB may name another build of the same source (used to check, on
+    the CPU, that the pins fail on a deliberately broken copy)."""
+    if force or not os.path.exists(LIB_PATH):
+        tmp = LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+               "-Wall", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    build(force=False)
+    lib = ctypes.CDLL(LIB_PATH)
+    c_u8p = ctypes.POINTER(ctypes.c_uint8)
+    c_i32p = ctypes.POINTER(ctypes.c_int32)
+    c_i64p = ctypes.POINTER(ctypes.c_int64)
+    c_f32p = ctypes.POINTER(ctypes.c_float)
+    c_f64p = ctypes.POINTER(ctypes.c_double)
+    c_u16p = ctypes.POINTER(ctypes.c_uint16)
+    lib.oracle_e2m1_decode.argtypes = [ctypes.c_int]
+    lib.oracle_e2m1_decode.restype = ctypes.c_double
+    lib.oracle_e2m1_encode.argtypes = [ctypes.c_float]
+    lib.oracle_e2m1_encode.restype = ctypes.c_int
+    lib.oracle_e4m3_decode.argtypes = [ctypes.c_int]
+    lib.oracle_e4m3_decode.restype = ctypes.c_double
+    lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+    lib.oracle_e4m3_encode.restype = ctypes.c_int
+    lib.oracle_bf16_bits_from_double.argtypes = [ctypes.c_double]
+    lib.oracle_bf16_bits_from_double.restype = ctypes.c_uint16
+    lib.oracle_quantize.argtypes = [c_f32p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                    c_f32p, ctypes.c_int, c_u8p, c_u8p]
+    lib.oracle_quantize.restype = ctypes.c_int
+    common = [c_u8p, c_u8p, ctypes.c_float, ctypes.c_int64, c_i32p, c_u8p, c_u8p, c_f32p,
+              c_i32p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+              c_i64p, ctypes.c_int64]
+    lib.oracle_grouped_gemm_exact.argtypes = common + [c_f64p, c_u16p]
+    lib.oracle_grouped_gemm_exact.restype = ctypes.c_int
+    lib.oracle_grouped_gemm_f64.argtypes = common + [c_f64p]
+    lib.oracle_grouped_gemm_f64.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a, ctype):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+# ------------------------------------------------------------------ codecs --
+
+def e2m1_decode(code: int) -> float:
+    return _load().oracle_e2m1_decode(int(code))
+
+
+def e2m1_encode(y: float) -> int:
+    return _load().oracle_e2m1_encode(float(y))
+
+
+def e4m3_decode(code: int) -> float:
+    return _load().oracle_e4m3_decode(int(code))
+
+
+def e4m3_encode(r: float) -> int:
+    return _load().oracle_e4m3_encode(float(r))
+
+
+def e2m1_encode_array(y: np.ndarray) -> np.ndarray:
+    f = _load().oracle_e2m1_encode
+    return np.array([f(float(v)) for v in np.asarray(y, dtype=np.float32).ravel()],
+                    dtype=np.uint8).reshape(np.shape(y))
+
+
+def e4m3_encode_array(r: np.ndarray) -> np.ndarray:
+    f = _load().oracle_e4m3_encode
+    return np.array([f(float(v)) for v in np.asarray(r, dtype=np.float32).ravel()],
+                    dtype=np.uint8).reshape(np.shape(r))
+
+
+def bf16_bits(x: float) -> int:
+    return _load().oracle_bf16_bits_from_double(float(x))
+
+
+def bf16_bits_array(x: np.ndarray) -> np.ndarray:
+    f = _load().oracle_bf16_bits_from_double
+    return np.array([f(float(v)) for v in np.asarray(x, dtype=np.float64).ravel()],
+                    dtype=np.uint16).reshape(np.shape(x))
+
+
+def bf16_bits_to_float(bits: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bit patterns to float32 (exact)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32)
+
+
+# ---------------------------------------------------------------- quantise --
+
+def quantize(x: np.ndarray, g: float | None = None):
+    """NVFP4-quantise a float32 matrix [rows][k].
+
+    g None -> dynamic tensor scale (computed and returned); else static g.
+    Returns (q uint8[rows][k/2], sf uint8[rows][k/16], g float32).
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.ndim != 2:
+        raise ValueError("x must be 2-D")
+    rows, k = x.shape
+    if k % 16:
+        raise ValueError("k must be a multiple of 16")
+    q = np.zeros((rows, k // 2), dtype=np.uint8)
+    sf = np.zeros((rows, k // 16), dtype=np.uint8)
+    gbuf = np.array([0.0 if g is None else g], dtype=np.float32)
+    rc = _load().oracle_quantize(_ptr(x, ctypes.c_float), rows, k, k, _ptr(gbuf, ctypes.c_float),
+                                 1 if g is None else 0, _ptr(q, ctypes.c_uint8),
+                                 _ptr(sf, ctypes.c_uint8))
+    if rc != 0:
+        raise ValueError("oracle_quantize rejected its arguments")
+    return q, sf, np.float32(gbuf[0])
+
+
+# ------------------------------------------------------------ grouped GEMM --
+
+def _gemm_args(a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets, a_row_index, rows_sel):
+    a_q = np.ascontiguousarray(a_q, dtype=np.uint8)
+    a_sf = np.ascontiguousarray(a_sf, dtype=np.uint8)
+    w_q = np.ascontiguousarray(w_q, dtype=np.uint8)
+    w_sf = np.ascontiguousarray(w_sf, dtype=np.uint8)
+    w_scale = np.ascontiguousarray(w_scale, dtype=np.float32)
+    offsets = np.ascontiguousarray(offsets, dtype=np.int32)
+    E, n, kb = w_q.shape
+    k = kb * 2
+    m_total = int(offsets[-1])
+    if a_row_index is not None:
+        a_row_index = np.ascontiguousarray(a_row_index, dtype=np.int32)
+    if rows_sel is not None:
+        rows_sel = np.ascontiguousarray(rows_sel, dtype=np.int64)
+        nsel = rows_sel.shape[0]
+    else:
+        nsel = m_total
+    return (a_q, a_sf, float(a_scale), w_q, w_sf, w_scale, offsets, a_row_index, rows_sel,
+            E, n, k, m_total, nsel)
+
+
+def grouped_gemm(a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets, a_row_index=None,
+                 rows_sel=None):
+    """Exact grouped GEMM.  Returns (R float64 [nsel][n], out_bf16_bits uint16 [nsel][n])."""
+    (a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets, a_row_index, rows_sel,
+     E, n, k, m_total, nsel) = _gemm_args(a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets,
+                                          a_row_index, rows_sel)
+    R = np.zeros((nsel, n), dtype=np.float64)
+    out = np.zeros((nsel, n), dtype=np.uint16)
+    rc = _load().oracle_grouped_gemm_exact(
+        _ptr(a_q, ctypes.c_uint8), _ptr(a_sf, ctypes.c_uint8), a_scale, a_q.shape[0],
+        _ptr(a_row_index, ctypes.c_int32), _ptr(w_q, ctypes.c_uint8), _ptr(w_sf, ctypes.c_uint8),
+        _ptr(w_scale, ctypes.c_float), _ptr(offsets, ctypes.c_int32), E, m_total, n, k,
+        _ptr(rows_sel, ctypes.c_int64), nsel, _ptr(R, ctypes.c_double), _ptr(out, ctypes.c_uint16))
+    if rc != 0:
+        raise ValueError("oracle_grouped_gemm_exact rejected its arguments")
+    return R, out
+
+
+def grouped_gemm_f64(a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets, a_row_index=None,
+                     rows_sel=None):
+    """FP64-accumulating evaluation of the same definition.  Returns R float64 [nsel][n]."""
+    (a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets, a_row_index, rows_sel,
+     E, n, k, m_total, nsel) = _gemm_args(a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets,
+                                          a_row_index, rows_sel)
+    R = np.zeros((nsel, n), dtype=np.float64)
+    rc = _load().oracle_grouped_gemm_f64(
+        _ptr(a_q, ctypes.c_uint8), _ptr(a_sf, ctypes.c_uint8), a_scale, a_q.shape[0],
+        _ptr(a_row_index, ctypes.c_int32), _ptr(w_q, ctypes.c_uint8), _ptr(w_sf, ctypes.c_uint8),
+        _ptr(w_scale, ctypes.c_float), _ptr(offsets, ctypes.c_int32), E, m_total, n, k,
+        _ptr(rows_sel, ctypes.c_int64), nsel, _ptr(R, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle_grouped_gemm_f64 rejected its arguments")
+    return R
+
+
+def row_error(got_bf16_bits: np.ndarray, ref_bf16_bits: np.ndarray, R: np.ndarray):
+    """Per-row relative error of a BF16 result against the oracle.
+
+    err[r] = ||got[r] - ref[r]||_2 / ||R[r]||_2 where ref = bf16(R) (the oracle's rounded
+    output) and R the unrounded oracle value; 0 when both rows are zero, inf when the
+    reference row is zero but the result is not.  Returns (err, ||R[r]||_2).
+    """
+    ref = bf16_bits_to_float(ref_bf16_bits).astype(np.float64)
+    got = bf16_bits_to_float(got_bf16_bits).astype(np.float64)
+    diff = np.linalg.norm(got - ref, axis=1)
+    norm = np.linalg.norm(R, axis=1)
+    safe = np.where(norm > 0, norm, 1.0)
+    err = np.where(norm > 0, diff / safe, np.where(diff > 0, np.inf, 0.0))
+    return err, norm
