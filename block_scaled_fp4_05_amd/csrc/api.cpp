@@ -1,0 +1,141 @@
+// C ABI of the NVFP4 MoE grouped GEMM library (declared in include/moe_fp4.h).
+//
+// Every entry point validates its arguments on the host before touching the
+// HIP runtime, so an argument that fails here never reaches a launch, and one
+// that passes here always launches: there is no second check that could reject
+// a configuration the first one accepted (the failure mode described on
+// "Peering into the CUTLASS SharedStorage", section "Why This Message Was
+// Written", where can_implement passed and initialize then failed).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "../../include/moe_fp4.h"
+#include "launch.h"
+
+using moe_fp4::GemmArgs;
+using moe_fp4::GemmTile;
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+constexpr int32_t kMaxExperts = 16384;  // the work-list prefix lives in LDS
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_gemm_shape(int32_t num_experts, int64_t m_total, int64_t n, int64_t k) {
+  if (num_experts < 1 || m_total < 0 || n < 1 || k < 1) return MOE_FP4_ERR_SHAPE;
+  if (num_experts > kMaxExperts) return MOE_FP4_ERR_UNSUPPORTED;
+  if (n % 16 != 0 || k % moe_fp4::kKStep != 0) return MOE_FP4_ERR_UNSUPPORTED;
+  if (n > INT32_MAX / 2 || m_total > INT32_MAX) return MOE_FP4_ERR_UNSUPPORTED;
+  // The work-list counts items in int32: bound the largest possible count.
+  const int64_t max_mtiles = m_total / 16 + (m_total < num_experts ? m_total : num_experts);
+  const int64_t n_tiles = (n + 31) / 32;
+  if (max_mtiles * n_tiles >= (int64_t)INT32_MAX) return MOE_FP4_ERR_UNSUPPORTED;
+  return MOE_FP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_fp4_abi_version(void) { return kAbiVersion; }
+
+const char* moe_fp4_status_string(int status) {
+  switch (status) {
+    case MOE_FP4_OK: return "ok";
+    case MOE_FP4_ERR_NULL: return "a required pointer is NULL";
+    case MOE_FP4_ERR_SHAPE: return "a size is out of range or sizes are inconsistent";
+    case MOE_FP4_ERR_ALIGN: return "a pointer or leading dimension is misaligned";
+    case MOE_FP4_ERR_UNSUPPORTED: return "valid arguments outside what the kernels support";
+    case MOE_FP4_ERR_HIP: return "the HIP runtime reported an error";
+    case MOE_FP4_ERR_ARG: return "an enumerated argument has an unknown value";
+    default: return "unknown status";
+  }
+}
+
+int64_t moe_fp4_stage_bytes(int64_t bm, int64_t bn, int64_t bk) {
+  if (bm < 1 || bn < 1 || bk < 16 || bk % 16 != 0) return -1;
+  // Packed FP4 (half a byte per element) plus one E4M3 byte per 16 elements,
+  // for the A tile (bm x bk) and the B tile (bn x bk).
+  const int64_t a = bm * bk / 2 + bm * (bk / 16);
+  const int64_t b = bn * bk / 2 + bn * (bk / 16);
+  return a + b;
+}
+
+int moe_fp4_quantize(const void* x, int in_dtype, int64_t rows, int64_t k, int64_t ld_x,
+                     uint8_t* q, uint8_t* sf, float* tensor_scale, int scale_mode,
+                     void* stream) {
+  if (in_dtype != MOE_FP4_IN_BF16 && in_dtype != MOE_FP4_IN_FP32) return MOE_FP4_ERR_ARG;
+  if (scale_mode != MOE_FP4_SCALE_STATIC && scale_mode != MOE_FP4_SCALE_DYNAMIC)
+    return MOE_FP4_ERR_ARG;
+  if (!tensor_scale) return MOE_FP4_ERR_NULL;
+  if (rows < 0 || k <= 0 || k % 16 != 0 || ld_x < k) return MOE_FP4_ERR_SHAPE;
+  if (rows > 0 && (!x || !q || !sf)) return MOE_FP4_ERR_NULL;
+  const int64_t esize = in_dtype == MOE_FP4_IN_BF16 ? 2 : 4;
+  if (!aligned(tensor_scale, 4)) return MOE_FP4_ERR_ALIGN;
+  if (rows > 0 && (!aligned(x, 16) || (ld_x * esize) % 16 != 0 || !aligned(q, 8)))
+    return MOE_FP4_ERR_ALIGN;
+  if (rows > 0 && (rows > INT64_MAX / k)) return MOE_FP4_ERR_SHAPE;
+  hipError_t err = moe_fp4::launch_quantize(x, in_dtype, rows, k, ld_x, q, sf, tensor_scale,
+                                            scale_mode == MOE_FP4_SCALE_DYNAMIC ? 1 : 0,
+                                            reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? MOE_FP4_OK : MOE_FP4_ERR_HIP;
+}
+
+int moe_grouped_gemm_fp4_plan(int32_t num_experts, int64_t m_total, int64_t n, int64_t k,
+                              moe_fp4_gemm_plan* plan) {
+  if (!plan) return MOE_FP4_ERR_NULL;
+  const int s = check_gemm_shape(num_experts, m_total, n, k);
+  if (s != MOE_FP4_OK) return s;
+  const GemmTile t = moe_fp4::choose_tile(num_experts, m_total, n, k, getenv("MOE_FP4_TILE"));
+  plan->tile_m = 16 * t.m_blocks;
+  plan->tile_n = 16 * t.n_blocks;
+  plan->k_step = moe_fp4::kKStep;
+  plan->waves_per_group = t.waves;
+  plan->lds_bytes = moe_fp4::gemm_lds_bytes(t, num_experts);
+  return MOE_FP4_OK;
+}
+
+int moe_grouped_gemm_fp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a_scale,
+                         int64_t a_rows, const int32_t* a_row_index,
+                         const uint8_t* w_q, const uint8_t* w_sf, const float* w_scale,
+                         const int32_t* expert_offsets, int32_t num_experts,
+                         int64_t m_total, int64_t n, int64_t k,
+                         uint16_t* out, int64_t ldo, void* stream) {
+  if (!a_q || !a_sf || !a_scale || !w_q || !w_sf || !w_scale || !expert_offsets || !out)
+    return MOE_FP4_ERR_NULL;
+  if (num_experts < 1 || m_total < 0 || n < 1 || k < 1 || ldo < n || a_rows < 0)
+    return MOE_FP4_ERR_SHAPE;
+  if (!a_row_index && a_rows < m_total) return MOE_FP4_ERR_SHAPE;
+  if (m_total > 0 && a_rows < 1) return MOE_FP4_ERR_SHAPE;
+  const int s = check_gemm_shape(num_experts, m_total, n, k);
+  if (s != MOE_FP4_OK) return s;
+  if (!aligned(a_q, 16) || !aligned(a_sf, 16) || !aligned(w_q, 16) || !aligned(w_sf, 16) ||
+      !aligned(out, 16) || !aligned(a_scale, 4) || !aligned(w_scale, 4) ||
+      !aligned(expert_offsets, 4) || (a_row_index && !aligned(a_row_index, 4)) || ldo % 8 != 0)
+    return MOE_FP4_ERR_ALIGN;
+  if (m_total == 0) return MOE_FP4_OK;
+  const GemmTile t = moe_fp4::choose_tile(num_experts, m_total, n, k, getenv("MOE_FP4_TILE"));
+  GemmArgs p;
+  p.a_q = a_q;
+  p.a_sf = a_sf;
+  p.a_scale = a_scale;
+  p.a_row_index = a_row_index;
+  p.w_q = w_q;
+  p.w_sf = w_sf;
+  p.w_scale = w_scale;
+  p.offsets = expert_offsets;
+  p.out = out;
+  p.a_rows = a_rows;
+  p.m_total = m_total;
+  p.n = n;
+  p.k = k;
+  p.ldo = ldo;
+  p.num_experts = num_experts;
+  p.n_tiles = (int32_t)((n + 16 * t.n_blocks - 1) / (16 * t.n_blocks));
+  hipError_t err = moe_fp4::launch_grouped_gemm(p, t, reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? MOE_FP4_OK : MOE_FP4_ERR_HIP;
+}
+
+}  // extern "C"

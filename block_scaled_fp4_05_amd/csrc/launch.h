@@ -1,0 +1,54 @@
+// Internal interface between the C-ABI layer (api.cpp) and the kernel
+// launchers.  Arguments reaching a launcher have been validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe_fp4 {
+
+// Quantiser: enqueue the kernels of moe_fp4_quantize on `stream`.
+hipError_t launch_quantize(const void* x, int in_dtype, int64_t rows, int64_t k, int64_t ld_x,
+                           uint8_t* q, uint8_t* sf, float* tensor_scale, int dynamic,
+                           hipStream_t stream);
+
+// Tile shapes of the grouped GEMM.  Rows per work item = 16 * m_blocks; output
+// columns per wavefront = 16 * n_blocks; a workgroup holds `waves` wavefronts,
+// each working on its own item.
+struct GemmTile {
+  int m_blocks;
+  int n_blocks;
+  int waves;
+};
+
+constexpr int kKStep = 256;  // K elements consumed per main-loop iteration
+
+// The tile used for a problem with these sizes; `env` (may be NULL) is the
+// value of MOE_FP4_TILE ("MxN" with M rows per item and N columns per wave).
+GemmTile choose_tile(int32_t num_experts, int64_t m_total, int64_t n, int64_t k, const char* env);
+
+// LDS bytes a workgroup of the grouped GEMM uses for `num_experts` experts.
+int64_t gemm_lds_bytes(const GemmTile& t, int32_t num_experts);
+
+struct GemmArgs {
+  const uint8_t* a_q;
+  const uint8_t* a_sf;
+  const float* a_scale;
+  const int32_t* a_row_index;
+  const uint8_t* w_q;
+  const uint8_t* w_sf;
+  const float* w_scale;
+  const int32_t* offsets;
+  uint16_t* out;
+  int64_t a_rows;
+  int64_t m_total;
+  int64_t n;
+  int64_t k;
+  int64_t ldo;
+  int32_t num_experts;
+  int32_t n_tiles;  // ceil(n / (16 * n_blocks))
+};
+
+hipError_t launch_grouped_gemm(const GemmArgs& args, const GemmTile& tile, hipStream_t stream);
+
+}  // namespace moe_fp4

@@ -1,0 +1,161 @@
+// NVFP4 activation quantiser for gfx950.
+//
+// Packing (two 4-bit values per byte) and the 16-element FP8 block scale come
+// from "Peering into the CUTLASS SharedStorage", section "Input Knowledge",
+// item 3; the recipe (tensor scale amax / 2688, round-to-nearest-even block
+// scale, IEEE division, round-to-nearest-even E2M1 code) is this library's
+// definition, stated in moe_fp4.h.
+//
+// Kernels, in stream order:
+//   DYNAMIC: reset -> amax -> quantize (derives g from amax) -> finalize (g in place)
+//   STATIC:  quantize (reads g)
+// The amax is accumulated in the caller's tensor_scale float itself (as the bit
+// pattern of a non-negative float, for which unsigned max is float max), so no
+// scratch memory is needed, and the reset is a kernel rather than a memset.
+//
+// One thread quantises one 16-element block: 32 (BF16) or 64 (FP32) bytes in,
+// 8 bytes of codes and 1 scale byte out, consecutive threads on consecutive
+// blocks of a row, so every access is coalesced.  The pass is HBM-bound:
+// (2 or 4) + 0.5625 bytes per element.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp4_device.h"
+#include "launch.h"
+
+namespace moe_fp4 {
+namespace {
+
+constexpr int kThreads = 256;
+
+// Sixteen consecutive input elements as floats (BF16 widens exactly).
+template <int DT>
+__device__ __forceinline__ void load_block16(const void* x, int64_t row, int64_t ld_x, int64_t b,
+                                             float (&v)[16]) {
+  if (DT == 0) {  // BF16
+    const uint8_t* p = reinterpret_cast<const uint8_t*>(x) + (row * ld_x + b * 16) * 2;
+    u32x4_t w0 = load_16B(p), w1 = load_16B(p + 16);
+    uint32_t w[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+      v[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
+    }
+  } else {  // FP32
+    const uint8_t* p = reinterpret_cast<const uint8_t*>(x) + (row * ld_x + b * 16) * 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4_t w = load_16B(p + 16 * j);
+      // Copy each lane to a scalar before the bit cast: a bit cast applied to
+      // a vector-element expression does not read the selected lane.
+      const uint32_t u[4] = {w[0], w[1], w[2], w[3]};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[4 * j + i] = __builtin_bit_cast(float, u[i]);
+    }
+  }
+}
+
+__global__ void k_amax_reset(float* ts) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *reinterpret_cast<uint32_t*>(ts) = 0u;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_amax(const void* x, int64_t rows, int64_t k,
+                                                   int64_t ld_x, float* ts) {
+  const int64_t nb = k / 16;
+  const int64_t total = rows * nb;
+  float m = 0.0f;
+  for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < total;
+       blk += (int64_t)gridDim.x * kThreads) {
+    float v[16];
+    load_block16<DT>(x, blk / nb, ld_x, blk % nb, v);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
+  if ((threadIdx.x & 63) == 0 && m > 0.0f)
+    atomicMax(reinterpret_cast<uint32_t*>(ts), __builtin_bit_cast(uint32_t, m));
+}
+
+// Tensor scale from the accumulated amax (DYNAMIC) or as given (STATIC).
+template <bool DYN>
+__device__ __forceinline__ float tensor_scale_of(const float* ts) {
+  const float t = *ts;
+  if (!DYN) return t;
+  return t > 0.0f ? t / 2688.0f : 1.0f;
+}
+
+template <int DT, bool DYN>
+__global__ __launch_bounds__(kThreads) void k_quantize(const void* x, int64_t rows, int64_t k,
+                                                       int64_t ld_x, uint8_t* q, uint8_t* sf,
+                                                       const float* ts) {
+  const float g = tensor_scale_of<DYN>(ts);
+  const float six_g = 6.0f * g;
+  const int64_t nb = k / 16;
+  const int64_t total = rows * nb;
+  for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < total;
+       blk += (int64_t)gridDim.x * kThreads) {
+    const int64_t row = blk / nb, b = blk % nb;
+    float v[16];
+    load_block16<DT>(x, row, ld_x, b, v);
+    float amax_b = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax_b = fmaxf(amax_b, fabsf(v[i]));
+    // Block scale: E4M3 with round-to-nearest-even.  The hardware conversion
+    // rounds to nearest even; clamping to 448 first makes it saturate.
+    const float r = fminf(amax_b / six_g, 448.0f);
+    const uint32_t sfb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(r, r, 0, false) & 0xFFu;
+    const float s = __builtin_amdgcn_cvt_f32_fp8(sfb, 0) * g;
+    uint32_t packed[2] = {0u, 0u};
+    if (s != 0.0f) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        // IEEE division (the compiler's correctly rounded sequence), then the
+        // hardware E2M1 conversion: nearest even, saturating, sign kept.
+        const float y0 = v[2 * i] / s, y1 = v[2 * i + 1] / s;
+        const uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y0, y1, 1.0f, 0) & 0xFFu;
+        packed[i >> 2] |= c << (8 * (i & 3));
+      }
+    }
+    *reinterpret_cast<u32x2_t*>(q + row * (k / 2) + b * 8) = u32x2_t{packed[0], packed[1]};
+    sf[row * nb + b] = (uint8_t)sfb;
+  }
+}
+
+__global__ void k_amax_finalize(float* ts) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *ts = tensor_scale_of<true>(ts);
+}
+
+template <int DT>
+hipError_t launch_dt(const void* x, int64_t rows, int64_t k, int64_t ld_x, uint8_t* q, uint8_t* sf,
+                     float* ts, int dynamic, hipStream_t stream) {
+  const int64_t total = rows * (k / 16);
+  const int64_t want = (total + kThreads - 1) / kThreads;
+  const int grid = (int)(want < 65536 ? (want > 0 ? want : 1) : 65536);
+  if (dynamic) {
+    hipLaunchKernelGGL(k_amax_reset, dim3(1), dim3(64), 0, stream, ts);
+    if (total > 0) {
+      const int agrid = grid < 2048 ? grid : 2048;
+      hipLaunchKernelGGL((k_amax<DT>), dim3(agrid), dim3(kThreads), 0, stream, x, rows, k, ld_x, ts);
+      hipLaunchKernelGGL((k_quantize<DT, true>), dim3(grid), dim3(kThreads), 0, stream, x, rows, k,
+                         ld_x, q, sf, (const float*)ts);
+    }
+    hipLaunchKernelGGL(k_amax_finalize, dim3(1), dim3(64), 0, stream, ts);
+  } else if (total > 0) {
+    hipLaunchKernelGGL((k_quantize<DT, false>), dim3(grid), dim3(kThreads), 0, stream, x, rows, k,
+                       ld_x, q, sf, (const float*)ts);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void* x, int in_dtype, int64_t rows, int64_t k, int64_t ld_x,
+                           uint8_t* q, uint8_t* sf, float* tensor_scale, int dynamic,
+                           hipStream_t stream) {
+  if (in_dtype == 0) return launch_dt<0>(x, rows, k, ld_x, q, sf, tensor_scale, dynamic, stream);
+  return launch_dt<1>(x, rows, k, ld_x, q, sf, tensor_scale, dynamic, stream);
+}
+
+}  // namespace moe_fp4

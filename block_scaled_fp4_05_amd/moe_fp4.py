@@ -1,0 +1,159 @@
+"""Python binding of libmoe_fp4.so (the C ABI in include/moe_fp4.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels.  PyTorch supplies device memory and the current stream.  If the
+compiled library is missing the calls raise; there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_fp4.so")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_HIP, ERR_ARG = range(7)
+IN_BF16, IN_FP32 = 0, 1
+SCALE_STATIC, SCALE_DYNAMIC = 0, 1
+
+# Every symbol include/moe_fp4.h declares.
+EXPORTED = ("moe_fp4_quantize", "moe_grouped_gemm_fp4", "moe_grouped_gemm_fp4_plan",
+            "moe_fp4_stage_bytes", "moe_fp4_status_string", "moe_fp4_abi_version")
+
+
+class MoeFp4Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
+                ("k_step", ctypes.c_int32), ("waves_per_group", ctypes.c_int32),
+                ("lds_bytes", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the compiled library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with block_scaled_fp4_05_amd.build")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, i = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
+    L.moe_fp4_quantize.argtypes = [vp, i, i64, i64, i64, vp, vp, vp, i, vp]
+    L.moe_fp4_quantize.restype = i
+    L.moe_grouped_gemm_fp4.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp, vp, i32, i64, i64, i64,
+                                       vp, i64, vp]
+    L.moe_grouped_gemm_fp4.restype = i
+    L.moe_grouped_gemm_fp4_plan.argtypes = [i32, i64, i64, i64, ctypes.POINTER(Plan)]
+    L.moe_grouped_gemm_fp4_plan.restype = i
+    L.moe_fp4_stage_bytes.argtypes = [i64, i64, i64]
+    L.moe_fp4_stage_bytes.restype = i64
+    L.moe_fp4_status_string.argtypes = [i]
+    L.moe_fp4_status_string.restype = ctypes.c_char_p
+    L.moe_fp4_abi_version.argtypes = []
+    L.moe_fp4_abi_version.restype = i
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().moe_fp4_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return lib().moe_fp4_abi_version()
+
+
+def stage_bytes(bm: int, bn: int, bk: int) -> int:
+    return lib().moe_fp4_stage_bytes(bm, bn, bk)
+
+
+def plan(num_experts: int, m_total: int, n: int, k: int) -> dict:
+    p = Plan()
+    st = lib().moe_grouped_gemm_fp4_plan(num_experts, m_total, n, k, ctypes.byref(p))
+    if st != OK:
+        raise MoeFp4Error(st, "moe_grouped_gemm_fp4_plan")
+    return {f: getattr(p, f) for f, _ in Plan._fields_}
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def quantize_raw(x_ptr, in_dtype, rows, k, ld_x, q_ptr, sf_ptr, scale_ptr, scale_mode, stream_ptr):
+    """Direct call with raw pointers; returns the status code."""
+    return lib().moe_fp4_quantize(x_ptr, in_dtype, rows, k, ld_x, q_ptr, sf_ptr, scale_ptr,
+                                  scale_mode, stream_ptr)
+
+
+def gemm_raw(*args):
+    """Direct call with raw pointers (C argument order); returns the status code."""
+    return lib().moe_grouped_gemm_fp4(*args)
+
+
+def quantize(x: torch.Tensor, tensor_scale: torch.Tensor | None = None, q=None, sf=None,
+             stream=None):
+    """NVFP4-quantise a 2-D BF16 or FP32 CUDA tensor [rows][k].
+
+    tensor_scale None -> dynamic: a new 1-element float32 tensor receives g.
+    Otherwise a 1-element float32 CUDA tensor holding a calibrated g (static).
+    Returns (q uint8[rows][k/2], sf uint8[rows][k/16], tensor_scale float32[1]).
+    """
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    if x.dtype == torch.bfloat16:
+        dt = IN_BF16
+    elif x.dtype == torch.float32:
+        dt = IN_FP32
+    else:
+        raise ValueError("x must be bfloat16 or float32")
+    rows, k = x.shape
+    dev = x.device
+    if q is None:
+        q = torch.empty((rows, k // 2), dtype=torch.uint8, device=dev)
+    if sf is None:
+        sf = torch.empty((rows, k // 16), dtype=torch.uint8, device=dev)
+    mode = SCALE_STATIC
+    if tensor_scale is None:
+        tensor_scale = torch.empty(1, dtype=torch.float32, device=dev)
+        mode = SCALE_DYNAMIC
+    st = lib().moe_fp4_quantize(_ptr(x), dt, rows, k, x.stride(0), _ptr(q), _ptr(sf),
+                                _ptr(tensor_scale), mode, _stream(stream))
+    if st != OK:
+        raise MoeFp4Error(st, "moe_fp4_quantize")
+    return q, sf, tensor_scale
+
+
+def grouped_gemm(a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets, a_row_index=None, out=None,
+                 m_total: int | None = None, stream=None):
+    """NVFP4 grouped GEMM.  Shapes: a_q [a_rows][k/2], a_sf [a_rows][k/16], a_scale [1],
+    w_q [E][n][k/2], w_sf [E][n][k/16], w_scale [E], offsets int32 [E+1],
+    a_row_index int32 [m_total] or None.  m_total defaults to a_row_index's length,
+    else a_rows.  Returns out, a BF16 tensor [m_total][n] (or the given `out`)."""
+    E, n, kb = w_q.shape
+    k = 2 * kb
+    a_rows = a_q.shape[0]
+    if m_total is None:
+        m_total = a_row_index.shape[0] if a_row_index is not None else a_rows
+    if out is None:
+        out = torch.empty((m_total, n), dtype=torch.bfloat16, device=w_q.device)
+    st = lib().moe_grouped_gemm_fp4(
+        _ptr(a_q), _ptr(a_sf), _ptr(a_scale), a_rows, _ptr(a_row_index), _ptr(w_q), _ptr(w_sf),
+        _ptr(w_scale), _ptr(offsets), E, m_total, n, k, _ptr(out), out.stride(0), _stream(stream))
+    if st != OK:
+        raise MoeFp4Error(st, "moe_grouped_gemm_fp4")
+    return out

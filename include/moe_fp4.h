@@ -1,0 +1,196 @@
+/*
+ * moe_fp4.h -- C ABI of the MI355X (gfx950) NVFP4 block-scaled MoE grouped GEMM.
+ *
+ * The operation: in Mixture-of-Experts decode, each expert's weight matrix is
+ * multiplied by the subset of tokens routed to it, so one launch serves many
+ * small GEMMs of variable height ("Peering into the CUTLASS Kernel Cache",
+ * section "Knowledge Required", the MoE grouped GEMM item; "Peering into the
+ * CUTLASS Kernel", section "Input Knowledge Required", item 4).  Operands are
+ * NVFP4: 4-bit values packed two per byte with one FP8 scale shared by each
+ * block of 16 elements ("Peering into the CUTLASS SharedStorage", section
+ * "Input Knowledge", item 3).  Tile M is the tokens of one expert, N the output
+ * features, K the reduction dimension (same page, item 5).  Accumulation is
+ * FP32 and the output BF16 (same page, "Why This Message Was Written", the
+ * epilogue staging estimate).
+ *
+ * Formats and conventions used by every entry point:
+ *   - FP4 element: E2M1 (OCP Microscaling v1.0): magnitudes 0, .5, 1, 1.5, 2,
+ *     3, 4, 6; bit 3 is the sign.  Element 2i of a row is the low nibble of
+ *     byte i, element 2i+1 the high nibble.
+ *   - Block scale: E4M3 (OCP OFP8 v1.0, no Inf, 0x7F/0xFF NaN), one per 16
+ *     consecutive elements along K, blocks starting at multiples of 16.
+ *   - Tensor scale: an FP32 decode multiplier.  An element's value is
+ *     E2M1(code) * E4M3(block scale) * tensor scale.  Activations have one
+ *     tensor scale; weights have one per expert.
+ *   - Matrices are row-major with K contiguous: activations q[rows][k/2],
+ *     sf[rows][k/16]; weights w_q[E][n][k/2], w_sf[E][n][k/16].
+ *
+ * Ownership: the caller owns every buffer; the library allocates no device
+ * memory, keeps no pointer after a call returns and holds no per-call state,
+ * so calls on different streams may run concurrently.
+ * Asynchrony: each call validates its arguments on the host, enqueues its
+ * kernels on `stream` (a hipStream_t; NULL = the default stream) and returns.
+ * A call that returns an error has enqueued nothing (except MOE_FP4_ERR_HIP,
+ * which reports a failed launch).  Results are visible after the stream
+ * synchronises.  Device pointers must be device (or managed) memory.
+ */
+#ifndef MOE_FP4_H
+#define MOE_FP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum {
+  MOE_FP4_OK = 0,
+  MOE_FP4_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  MOE_FP4_ERR_SHAPE = 2,       /* a size is out of range or sizes are inconsistent   */
+  MOE_FP4_ERR_ALIGN = 3,       /* a pointer or leading dimension is misaligned       */
+  MOE_FP4_ERR_UNSUPPORTED = 4, /* well-formed but outside what the kernels handle    */
+  MOE_FP4_ERR_HIP = 5,         /* the HIP runtime reported an error                  */
+  MOE_FP4_ERR_ARG = 6          /* an enumerated argument has an unknown value        */
+};
+
+/* Input element types of moe_fp4_quantize. */
+enum { MOE_FP4_IN_BF16 = 0, MOE_FP4_IN_FP32 = 1 };
+
+/* Tensor-scale modes of moe_fp4_quantize. */
+enum {
+  MOE_FP4_SCALE_STATIC = 0, /* use *tensor_scale as given (a calibrated scale, > 0)  */
+  MOE_FP4_SCALE_DYNAMIC = 1 /* compute it from the data and write it to *tensor_scale */
+};
+
+/*
+ * moe_fp4_quantize -- NVFP4-quantise a [rows][k] matrix (activations).
+ *
+ * The pages give the packing (two 4-bit values per byte) and the 16-element
+ * FP8 block scale ("Peering into the CUTLASS SharedStorage", "Input
+ * Knowledge", item 3) but not the recipe; this library defines it as follows,
+ * with fl() one IEEE binary32 operation rounded to nearest even and division a
+ * true division (not a reciprocal multiply):
+ *   1. tensor scale g: DYNAMIC: g = amax > 0 ? fl(amax / 2688) : 1, where amax
+ *      is the largest |x| of the whole matrix and 2688 = 6 * 448; written to
+ *      *tensor_scale.  STATIC: g = *tensor_scale.
+ *   2. per row, per block of 16: r = fl(max|x_block| / fl(6 g)),
+ *      sf = E4M3(r) rounded to nearest even, saturating at 448;
+ *      s = fl(E4M3value(sf) * g).
+ *   3. per element: y = (s == 0) ? +0 : fl(x / s); code = E2M1(y) rounded to
+ *      nearest even, saturating at 6; the sign bit is the sign of y.
+ * The result is bit-exact: the same q, sf and g bits on every run and stream.
+ *
+ *   x            device, [rows][ld_x] elements of in_dtype (BF16 or FP32); the
+ *                first k of each row are used.  16-byte aligned base, and
+ *                ld_x * sizeof(element) a multiple of 16.
+ *   in_dtype     MOE_FP4_IN_BF16 or MOE_FP4_IN_FP32.
+ *   rows         >= 0 (0 is a no-op apart from the DYNAMIC scale, which is 1).
+ *   k            > 0, a multiple of 16.
+ *   ld_x         >= k.
+ *   q            device, [rows][k/2] bytes, 8-byte aligned.
+ *   sf           device, [rows][k/16] bytes.
+ *   tensor_scale device, one float: input (STATIC, must be finite and > 0) or
+ *                output (DYNAMIC).  4-byte aligned.
+ *   scale_mode   MOE_FP4_SCALE_STATIC or MOE_FP4_SCALE_DYNAMIC.
+ *   stream       hipStream_t or NULL.
+ * Inputs must be finite; the result for NaN or Inf inputs is unspecified.
+ * Errors: NULL (x, q, sf or tensor_scale NULL with rows > 0; tensor_scale
+ * NULL always), SHAPE (rows < 0, k <= 0, k % 16, ld_x < k), ALIGN, ARG, HIP.
+ */
+int moe_fp4_quantize(const void* x, int in_dtype, int64_t rows, int64_t k, int64_t ld_x,
+                     uint8_t* q, uint8_t* sf, float* tensor_scale, int scale_mode,
+                     void* stream);
+
+/*
+ * moe_grouped_gemm_fp4 -- NVFP4 block-scaled grouped GEMM over experts.
+ *
+ * For each expert e and each output row r in [off[e], off[e+1]) and column
+ * j in [0, n):
+ *     out[r][j] = bf16( a_scale * w_scale[e] * sum_k A(src(r), k) * W(e, j, k) )
+ * where A(i, k) = E2M1(a_q code) * E4M3(a_sf[i][k/16]),
+ *       W(e, j, k) = E2M1(w_q code) * E4M3(w_sf[e][j][k/16]),
+ *       src(r) = a_row_index ? a_row_index[r] : r,
+ * the sum is accumulated in FP32 from exactly dequantised products, and bf16()
+ * rounds to nearest even.  Multiplying many expert GEMMs in one launch is the
+ * grouped problem of "Peering into the CUTLASS Kernel", "Input Knowledge
+ * Required", item 4.  Columns j >= n of `out` and rows outside
+ * [off[0], off[E]) are never written; an empty expert writes nothing.
+ *
+ *   a_q          device, [a_rows][k/2] packed activation codes, 16-byte aligned.
+ *   a_sf         device, [a_rows][k/16] activation block scales, 16-byte aligned.
+ *   a_scale      device, one float: activation tensor scale.
+ *   a_rows       rows of a_q / a_sf; >= m_total when a_row_index is NULL.
+ *   a_row_index  device, [m_total] int32 in [0, a_rows), or NULL for identity.
+ *                Lets rows be gathered in expert order without a copy (each
+ *                token quantised once, read once per expert it is routed to).
+ *   w_q          device, [num_experts][n][k/2] packed weight codes, 16-byte aligned.
+ *   w_sf         device, [num_experts][n][k/16] weight block scales, 16-byte aligned.
+ *   w_scale      device, [num_experts] floats: per-expert weight tensor scales.
+ *   expert_offsets device, [num_experts+1] int32, offsets[0] = 0, non-decreasing,
+ *                offsets[E] = m_total.  These are device-side preconditions, not
+ *                checked; the kernel clamps every offset into [0, m_total] and
+ *                every gathered row into [0, a_rows), so a violation cannot
+ *                read or write outside the buffers described here.
+ *   num_experts  >= 1.
+ *   m_total      >= 0 (0 is a no-op).
+ *   n            >= 1, a multiple of 16.
+ *   k            >= 1, a multiple of 256 (UNSUPPORTED otherwise).
+ *   out          device, [m_total][ldo] BF16 (uint16 bit patterns), 16-byte
+ *                aligned; ldo >= n and a multiple of 8.
+ *   stream       hipStream_t or NULL.
+ * No host synchronisation and no device allocation.  Deterministic: the same
+ * inputs give the same output bits (no atomics in the accumulation).
+ * Errors: NULL, SHAPE (num_experts < 1, m_total < 0, n < 1, k < 1, ldo < n,
+ * a_rows < m_total without an index, a_rows < 1 with m_total > 0),
+ * ALIGN, UNSUPPORTED (n % 16, k % 256), HIP.
+ */
+int moe_grouped_gemm_fp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a_scale,
+                         int64_t a_rows, const int32_t* a_row_index,
+                         const uint8_t* w_q, const uint8_t* w_sf, const float* w_scale,
+                         const int32_t* expert_offsets, int32_t num_experts,
+                         int64_t m_total, int64_t n, int64_t k,
+                         uint16_t* out, int64_t ldo, void* stream);
+
+/* Kernel configuration the GEMM picks for a problem (host-only, no GPU call). */
+typedef struct {
+  int32_t tile_m;          /* rows of one expert per work item                       */
+  int32_t tile_n;          /* output columns per work item                           */
+  int32_t k_step;          /* K elements per main-loop iteration                     */
+  int32_t waves_per_group; /* wavefronts (64 lanes) per workgroup                    */
+  int64_t lds_bytes;       /* LDS per workgroup                                      */
+} moe_fp4_gemm_plan;
+
+/*
+ * moe_grouped_gemm_fp4_plan -- the configuration moe_grouped_gemm_fp4 would use
+ * for these sizes (m_total / num_experts rows per expert on average).
+ * Returns MOE_FP4_OK, or NULL / SHAPE / UNSUPPORTED as the GEMM would.
+ * The MOE_FP4_TILE environment variable ("MxN", e.g. "32x64") overrides the
+ * choice of tile_m x tile_n when it names a supported tile.
+ */
+int moe_grouped_gemm_fp4_plan(int32_t num_experts, int64_t m_total, int64_t n, int64_t k,
+                              moe_fp4_gemm_plan* plan);
+
+/*
+ * moe_fp4_stage_bytes -- bytes one pipeline stage of a bm x bn x bk tile moves
+ * into on-chip memory: packed FP4 for both operands plus their E4M3 block
+ * scales, (bm + bn) * bk * (1/2 + 1/16).  This is the per-stage transaction
+ * count of the block-scaled mainloop printed on "Peering into the CUTLASS
+ * SharedStorage" (section "The Message": bytes of the A tile and its scales
+ * plus bytes of the B tile and its scales).  Returns -1 unless bm, bn >= 1 and
+ * bk is a positive multiple of 16.
+ */
+int64_t moe_fp4_stage_bytes(int64_t bm, int64_t bn, int64_t bk);
+
+/* Human-readable name of a status code (never NULL). */
+const char* moe_fp4_status_string(int status);
+
+/* ABI version: bumped whenever a signature or a layout above changes. */
+int moe_fp4_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FP4_H */

@@ -1,0 +1,124 @@
+"""GPU parity of moe_fp4_quantize: q, sf and the tensor-scale bits must equal the
+oracle's exactly, on the workloads' activations and on adversarial inputs."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import dev, require_gpu, say
+from oracle import oracle as orc
+from workloads import configs, gen
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(x32: np.ndarray, dtype: torch.dtype, static_g=None, ld_pad=0):
+    """Quantise on the GPU; x32 holds values exactly representable in `dtype`."""
+    from block_scaled_fp4_05_amd import moe_fp4
+    rows, k = x32.shape
+    buf = np.zeros((rows, k + ld_pad), np.float32)
+    buf[:, :k] = x32
+    xt = dev(buf).to(dtype)[:, :k]
+    ts = None if static_g is None else torch.tensor([static_g], dtype=torch.float32, device="cuda")
+    q, sf, g = moe_fp4.quantize(xt, ts)
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), sf.cpu().numpy(), np.float32(g.cpu().numpy()[0])
+
+
+def _check(x32, dtype, static_g=None, ld_pad=0, label=""):
+    say(f"quantize {label} shape={x32.shape} dtype={dtype} static_g={static_g} pad={ld_pad}")
+    q, sf, g = _run(x32, dtype, static_g, ld_pad)
+    oq, osf, og = orc.quantize(x32, g=static_g)
+    assert g.view(np.uint32) == np.float32(og).view(np.uint32), (g, og)
+    bad_sf = np.argwhere(sf != osf)
+    assert bad_sf.size == 0, f"{len(bad_sf)} scale bytes differ, first {bad_sf[:5].tolist()}"
+    bad_q = np.argwhere(q != oq)
+    assert bad_q.size == 0, f"{len(bad_q)} code bytes differ, first {bad_q[:5].tolist()}"
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+@pytest.mark.parametrize("name", ["c1", "c3", "c4", "c5"])
+def test_workload_activations_bit_exact(name):
+    w = configs.WORKLOADS[name]
+    x = configs.activations(w)
+    _check(x, torch.bfloat16, label=name)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("static_g", [None, 0.0123, 3.0e-4])
+def test_random_shapes(dtype, static_g):
+    rng = np.random.default_rng(17)
+    for rows, k in [(1, 16), (3, 48), (17, 272), (64, 1024), (257, 2064)]:
+        x = (rng.standard_normal((rows, k)) * 10.0 ** rng.uniform(-3, 3, (rows, 1))).astype(np.float32)
+        if dtype == torch.bfloat16:
+            x = gen.bf16_round(x)
+        _check(x, dtype, static_g, label=f"random {rows}x{k}")
+
+
+def test_padded_leading_dimension():
+    x = gen.bf16_round(gen.normal((33, 160), 5))
+    _check(x, torch.bfloat16, ld_pad=32, label="ld_x > k")
+    _check(gen.normal((9, 96), 6), torch.float32, ld_pad=4, label="ld_x > k fp32")
+
+
+def test_adversarial_blocks():
+    rng = np.random.default_rng(23)
+    k = 256
+    rows = []
+    rows.append(np.zeros(k))                                     # all-zero row
+    r = rng.standard_normal(k); r[::3] = -0.0; rows.append(r)    # signed zeros
+    r = rng.standard_normal(k) * 1e-4; rows.append(r)            # subnormal block scales
+    r = rng.standard_normal(k); r[5] = 1e4; rows.append(r)       # one saturating block
+    ties = np.array([6, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5, -0.25, -0.75, -1.25, -1.75, -2.5,
+                     -3.5, -5, 0.1])
+    rows.append(np.tile(ties, k // 16))                          # E2M1 midpoints
+    rows.append(np.tile(ties * 1.375 * 2 ** -5, k // 16))        # midpoints times an odd scale
+    r = np.ones(k) * 3.0e-41; rows.append(r)                     # subnormal inputs
+    x = np.array(rows, dtype=np.float32)
+    for g in (None, 1.0, 1.0e-3):
+        _check(x, torch.float32, g, label=f"adversarial g={g}")
+    _check(gen.bf16_round(x), torch.bfloat16, None, label="adversarial bf16")
+
+
+def test_threshold_rows_static_scale_one():
+    """Block scales with odd mantissas and elements on E2M1 thresholds +- ulps."""
+    rows = []
+    for v in (1.125 * 2 ** -2, 1.375 * 2 ** -5, 1.625, 1.875 * 2 ** 3, 1.75 * 2 ** 2):
+        for t in (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0):
+            base = np.float32(t * v)
+            row = [np.float32(6 * v)]
+            xx = base
+            for _ in range(7):
+                row.append(xx)
+                xx = np.nextafter(xx, np.float32(np.inf))
+            xx = np.nextafter(base, np.float32(-np.inf))
+            for _ in range(7):
+                row.append(xx)
+                xx = np.nextafter(xx, np.float32(-np.inf))
+            row.append(-base)
+            rows.append(row)
+    _check(np.array(rows, np.float32), torch.float32, 1.0, label="thresholds")
+
+
+def test_zero_rows_dynamic_scale_is_one():
+    from block_scaled_fp4_05_amd import moe_fp4
+    say("quantize rows=0 dynamic")
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    q, sf, g = moe_fp4.quantize(x)
+    torch.cuda.synchronize()
+    assert q.shape == (0, 32) and float(g.cpu()[0]) == 1.0
+
+
+def test_deterministic_and_stream_safe():
+    from block_scaled_fp4_05_amd import moe_fp4
+    x = dev(gen.bf16_round(gen.normal((512, 6144), 41))).to(torch.bfloat16)
+    say("quantize determinism on a side stream")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        q1, sf1, g1 = moe_fp4.quantize(x)
+        q2, sf2, g2 = moe_fp4.quantize(x)
+    s.synchronize()
+    assert torch.equal(q1, q2) and torch.equal(sf1, sf2) and torch.equal(g1, g2)
