@@ -1,0 +1,358 @@
+#!/usr/bin/env python3
+"""Throughput of the NVFP4 MoE hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic decode input:
+  1. moe_fp4_quantize: the step's BF16 token activations -> NVFP4 (dynamic
+     tensor scale), one row per token;
+  2. moe_grouped_gemm_fp4: every expert's GEMM over the tokens routed to it
+     (rows gathered through a row index), FP32 accumulation, BF16 output.
+Both run in the HIP library; inputs are resident in HBM before timing starts.
+
+Weights are rotated over several device copies so that each step streams
+weights that neither the L2 nor the 256 MB Infinity Cache holds (the decode
+case, where every layer's experts differ from the previous one's).
+
+Prints ONE JSON line (the value is whole-step TFLOP/s; the GEMM kernel's HBM
+roofline and the CPU oracle's throughput on the same workload ride along).
+
+  python bench.py [--steps K] [--warmup W] [--workload c3] [--secondary c4]
+  python bench.py --copy-calibration   # a plain copy of known size, for counter scaling
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "grouped FP4 GEMM TFLOPS & HBM GB/s (% roofline) at 16/32 tokens/expert"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, AMD published
+FP4_PEAK_TFLOPS = 10066.0       # dense MXFP4 MFMA, AMD published
+F16_PEAK_TFLOPS = 2516.6        # dense FP16 MFMA, AMD published
+ROTATE_BYTES = 1.0e9            # weight bytes cycled through between reuses
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_grouped_gemm.txt")
+GEMM_SOURCES = [os.path.join(ROOT, "block_scaled_fp4_05_amd", "csrc", f)
+                for f in ("grouped_gemm.hip", "fp4_device.h")]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c3", help="c1, c2, c3, c4, c5 or c5b (default c3)")
+    ap.add_argument("--secondary", default="c4",
+                    help="second workload reported in the same line ('none' to skip)")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a device copy of known size (counter scale factor)")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ inputs --
+
+def alg_bytes(w, offsets, tokens_used):
+    """Algorithmic HBM bytes of one grouped-GEMM launch: every non-empty expert's
+    packed weights and scales once, every distinct token row once, the row index,
+    the BF16 output, the offsets and the scales."""
+    import numpy as np
+    nz = int(np.count_nonzero(np.diff(offsets)))
+    m = int(offsets[-1])
+    per_elem = 0.5 + 1.0 / 16.0
+    wb = nz * w.n * w.k * per_elem
+    ab = tokens_used * w.k * per_elem
+    ob = 2.0 * m * w.n
+    misc = 4.0 * m + 4.0 * (w.experts + 1) + 4.0 * w.experts + 4.0
+    return wb + ab + ob + misc, dict(weights=wb, activations=ab, output=ob, index_offsets=misc,
+                                     nonempty_experts=nz)
+
+
+def quant_alg_bytes(tokens, k):
+    """Algorithmic bytes of the activation quantiser: BF16 in once, codes + scales out."""
+    return tokens * k * 2.0 + tokens * k * (0.5 + 1.0 / 16.0) + 4.0
+
+
+class Problem:
+    """Device-resident inputs of one workload (weights quantised on the GPU by
+    moe_fp4_quantize from the seeded FP32 weights)."""
+
+    def __init__(self, name, keep_host_weights=False):
+        import numpy as np
+        import torch
+        from block_scaled_fp4_05_amd import moe_fp4
+        from workloads import configs
+
+        w = configs.WORKLOADS[name]
+        self.w = w
+        dev = torch.device("cuda")
+        row_token, offsets = configs.routing(w)
+        self.row_token, self.offsets = row_token, offsets
+        self.m_total = int(offsets[-1])
+        x = configs.activations(w)
+        self.x_host = x
+        self.x = torch.from_numpy(x).to(dev).to(torch.bfloat16)
+        self.idx = torch.from_numpy(row_token).to(dev)
+        self.off = torch.from_numpy(offsets).to(dev)
+        E, n, k = w.experts, w.n, w.k
+        w_q = torch.empty((E, n, k // 2), dtype=torch.uint8, device=dev)
+        w_sf = torch.empty((E, n, k // 16), dtype=torch.uint8, device=dev)
+        w_scale = torch.empty(E, dtype=torch.float32, device=dev)
+        self.host_weights = [] if keep_host_weights else None
+        t0 = time.time()
+        for e in range(E):
+            we = configs.expert_weight(w, e)
+            if keep_host_weights:
+                self.host_weights.append(we)
+            wt = torch.from_numpy(we).to(dev)
+            moe_fp4.quantize(wt, tensor_scale=w_scale[e:e + 1], q=w_q[e], sf=w_sf[e], dynamic=True)
+        torch.cuda.synchronize()
+        log(f"{name}: weights quantised on the GPU in {time.time() - t0:.1f}s")
+        wbytes = E * n * k * (0.5 + 1.0 / 16.0)
+        copies = max(1, min(8, math.ceil(ROTATE_BYTES / wbytes)))
+        self.weights = [(w_q, w_sf, w_scale)]
+        for _ in range(copies - 1):
+            self.weights.append((w_q.clone(), w_sf.clone(), w_scale.clone()))
+        self.q = torch.empty((w.tokens, k // 2), dtype=torch.uint8, device=dev)
+        self.sf = torch.empty((w.tokens, k // 16), dtype=torch.uint8, device=dev)
+        self.g = torch.empty(1, dtype=torch.float32, device=dev)
+        self.out = torch.empty((self.m_total, n), dtype=torch.bfloat16, device=dev)
+        self.flops = 2.0 * self.m_total * n * k
+        self.gemm_bytes, self.gemm_bytes_parts = alg_bytes(w, offsets, len(np.unique(row_token)))
+        self.quant_bytes = quant_alg_bytes(w.tokens, k)
+        torch.cuda.synchronize()
+
+    def step(self, i, ev=None):
+        from block_scaled_fp4_05_amd import moe_fp4
+        w_q, w_sf, w_scale = self.weights[i % len(self.weights)]
+        if ev is not None:
+            ev[0].record()
+        moe_fp4.quantize(self.x, tensor_scale=self.g, q=self.q, sf=self.sf, dynamic=True)
+        if ev is not None:
+            ev[1].record()
+        moe_fp4.grouped_gemm(self.q, self.sf, self.g, w_q, w_sf, w_scale, self.off,
+                             a_row_index=self.idx, out=self.out, m_total=self.m_total)
+        if ev is not None:
+            ev[2].record()
+
+
+def measure(prob, steps, warmup):
+    """Time `steps` whole steps after `warmup` untimed ones.  Returns the wall time
+    per step and the per-kernel averages from HIP events on the launch stream."""
+    import torch
+    for i in range(warmup):
+        prob.step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        prob.step(warmup + i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    quant_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    gemm_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    region_ms = evs[0][0].elapsed_time(evs[-1][2])
+    return dict(wall_ms_per_step=(t1 - t0) * 1e3 / steps,
+                gpu_ms_per_step=region_ms / steps,
+                quant_ms=sum(quant_ms) / steps, gemm_ms=sum(gemm_ms) / steps,
+                gemm_ms_min=min(gemm_ms), gemm_ms_max=max(gemm_ms))
+
+
+def plan_of(prob):
+    from block_scaled_fp4_05_amd import moe_fp4
+    w = prob.w
+    return moe_fp4.plan(w.experts, prob.m_total, w.n, w.k)
+
+
+def summary(prob, r):
+    ms = r["wall_ms_per_step"]
+    gemm_s = r["gemm_ms"] * 1e-3
+    return dict(
+        workload=prob.w.name,
+        ms_per_step=round(ms, 4),
+        tflops_step=round(prob.flops / (ms * 1e-3) / 1e12, 2),
+        gbps_step=round((prob.gemm_bytes + prob.quant_bytes) / (ms * 1e-3) / 1e9, 1),
+        gemm_us=round(r["gemm_ms"] * 1e3, 2),
+        quantize_us=round(r["quant_ms"] * 1e3, 2),
+        gemm_tflops=round(prob.flops / gemm_s / 1e12, 2),
+        gemm_gbps=round(prob.gemm_bytes / gemm_s / 1e9, 1),
+        gemm_hbm_frac=round(prob.gemm_bytes / gemm_s / 1e9 / HBM_PEAK_GBS, 4),
+        gemm_fp4_peak_frac=round(prob.flops / gemm_s / 1e12 / FP4_PEAK_TFLOPS, 5),
+        gemm_f16_mfma_peak_frac=round(prob.flops / gemm_s / 1e12 / F16_PEAK_TFLOPS, 5),
+        tile=plan_of(prob),
+        weight_copies_rotated=len(prob.weights),
+    )
+
+
+# --------------------------------------------------------------- counters --
+
+def sources_digest():
+    h = hashlib.sha256()
+    for p in GEMM_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per grouped-GEMM launch from the committed counter summary, or None
+    when it is missing, for another workload, or taken on other kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.lstrip().startswith("#"):
+                key, v = line.split(":", 1)
+                vals[key.strip()] = v.strip()
+    try:
+        if vals.get("workload") != workload or vals.get("sources_sha256_16") != sources_digest():
+            return None
+        return float(vals["hbm_bytes_per_dispatch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ----------------------------------------------------------- CPU baseline --
+
+def cpu_baseline(prob):
+    """The oracle (plain C + OpenMP) on the same workload: quantise the step's
+    activations and run the whole grouped GEMM, timed on the host cores.  Its
+    weights come from the oracle's own quantiser on the same seeded FP32 weights."""
+    import numpy as np
+    from oracle import oracle as orc
+    w = prob.w
+    E, n, k = w.experts, w.n, w.k
+    w_q = np.empty((E, n, k // 2), np.uint8)
+    w_sf = np.empty((E, n, k // 16), np.uint8)
+    w_scale = np.empty(E, np.float32)
+    for e in range(E):
+        w_q[e], w_sf[e], w_scale[e] = orc.quantize(prob.host_weights[e])
+    t0 = time.perf_counter()
+    a_q, a_sf, a_scale = orc.quantize(prob.x_host)
+    t1 = time.perf_counter()
+    R, ref = orc.grouped_gemm(a_q, a_sf, a_scale, w_q, w_sf, w_scale, prob.offsets,
+                              a_row_index=prob.row_token)
+    t2 = time.perf_counter()
+    secs = t2 - t0
+    base = dict(value=round(prob.flops / secs / 1e12, 6), unit="TFLOPS", cores=orc.num_threads(),
+                kind="oracle",
+                sample=f"whole {w.name} step: quantise {w.tokens}x{k} activations + grouped GEMM "
+                       f"over all {prob.m_total} routed rows ({E} experts, N={n}, K={k}), once",
+                seconds=round(secs, 3), quantize_s=round(t1 - t0, 3), gemm_s=round(t2 - t1, 3))
+    return base, R, ref
+
+
+def parity(prob, R, ref):
+    """Row errors of the GPU output (last timed step) against the oracle's."""
+    import numpy as np
+    import torch
+    from oracle import oracle as orc
+    got = prob.out.view(torch.int16).cpu().numpy().view(np.uint16)
+    err, _ = orc.row_error(got, ref, R)
+    return dict(rows=int(err.size), max_row_err=float(err.max()), tol=2e-3,
+                ok=bool(np.all(err <= 2e-3)))
+
+
+# -------------------------------------------------------------------- main --
+
+def copy_calibration():
+    import torch
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": nbytes, "bytes_written": nbytes,
+                      "dispatches": 3}), flush=True)
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this path has no multi-GPU mode (each GPU would run "
+              "its own expert shard independently); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    from block_scaled_fp4_05_amd import moe_fp4
+    moe_fp4.lib()  # the HIP library must be built: there is no fallback
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    want_cpu = not args.no_cpu_baseline
+    prob = Problem(args.workload, keep_host_weights=want_cpu)
+    log(f"{args.workload}: {args.warmup} warmup + {args.steps} timed steps")
+    r = measure(prob, args.steps, args.warmup)
+    main_s = summary(prob, r)
+    log(json.dumps(main_s))
+
+    gemm_s = r["gemm_ms"] * 1e-3
+    achieved = prob.gemm_bytes / gemm_s / 1e9
+    traffic = measured_traffic(args.workload)
+    roof = {"bound": "hbm", "kernel": "k_grouped_gemm", "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic, "algorithmic_bytes": int(prob.gemm_bytes),
+            "avg_launch_us": round(r["gemm_ms"] * 1e3, 2)}
+
+    secondary = None
+    if args.secondary and args.secondary != "none" and args.secondary != args.workload:
+        p2 = Problem(args.secondary)
+        r2 = measure(p2, args.steps, args.warmup)
+        secondary = summary(p2, r2)
+        log(json.dumps(secondary))
+        del p2
+        torch.cuda.empty_cache()
+
+    base = None
+    par = None
+    if want_cpu:
+        log("timing the CPU oracle on the same workload")
+        base, R, ref = cpu_baseline(prob)
+        par = parity(prob, R, ref)
+
+    w = prob.w
+    line = {
+        "metric": METRIC,
+        "value": main_s["tflops_step"],
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_s["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4 (e2m1 x e4m3/16) -> exact f16 mfma, f32 acc, bf16 out",
+        "data": "synthetic (seeded N(0,1) activations and weights, seeded routing)",
+        "config": {"workload": f"{w.name}: {w.experts} experts, {w.tokens} tokens top-{w.topk} "
+                               f"({w.routing} routing), K={w.k}, N={w.n}",
+                   "experts": w.experts, "tokens": w.tokens, "topk": w.topk,
+                   "m_total": prob.m_total, "n": w.n, "k": w.k},
+        "hbm_gbps": main_s["gbps_step"],
+        "gemm": main_s,
+        "roofline": roof,
+        "cpu_baseline": base,
+        "parity_vs_oracle": par,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -28,10 +28,14 @@ int check_gemm_shape(int32_t num_experts, int64_t m_total, int64_t n, int64_t k)
   if (num_experts > kMaxExperts) return MOE_FP4_ERR_UNSUPPORTED;
   if (n % 16 != 0 || k % moe_fp4::kKStep != 0) return MOE_FP4_ERR_UNSUPPORTED;
   if (n > INT32_MAX / 2 || m_total > INT32_MAX) return MOE_FP4_ERR_UNSUPPORTED;
+  // One expert's packed weights are addressed with 32-bit buffer offsets.
+  if (n * (k / 2) > (int64_t)INT32_MAX - 4096) return MOE_FP4_ERR_UNSUPPORTED;
   // The work-list counts items in int32: bound the largest possible count.
   const int64_t max_mtiles = m_total / 16 + (m_total < num_experts ? m_total : num_experts);
   const int64_t n_tiles = (n + 31) / 32;
-  if (max_mtiles * n_tiles >= (int64_t)INT32_MAX) return MOE_FP4_ERR_UNSUPPORTED;
+  // Items and items x pipeline stages are counted in int32.
+  if (max_mtiles * n_tiles * (k / moe_fp4::kKStep) >= (int64_t)INT32_MAX)
+    return MOE_FP4_ERR_UNSUPPORTED;
   return MOE_FP4_OK;
 }
 
@@ -91,7 +95,7 @@ int moe_grouped_gemm_fp4_plan(int32_t num_experts, int64_t m_total, int64_t n, i
   const GemmTile t = moe_fp4::choose_tile(num_experts, m_total, n, k, getenv("MOE_FP4_TILE"));
   plan->tile_m = 16 * t.m_blocks;
   plan->tile_n = 16 * t.n_blocks;
-  plan->k_step = moe_fp4::kKStep;
+  plan->k_step = moe_fp4::kKStep * t.k_sub;
   plan->waves_per_group = t.waves;
   plan->lds_bytes = moe_fp4::gemm_lds_bytes(t, num_experts);
   return MOE_FP4_OK;
@@ -115,6 +119,10 @@ int moe_grouped_gemm_fp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a
       !aligned(out, 16) || !aligned(a_scale, 4) || !aligned(w_scale, 4) ||
       !aligned(expert_offsets, 4) || (a_row_index && !aligned(a_row_index, 4)) || ldo % 8 != 0)
     return MOE_FP4_ERR_ALIGN;
+  // Activations and one item's output rows are addressed with 32-bit buffer
+  // offsets as well.
+  if (a_rows * (k / 2) > (int64_t)INT32_MAX - 4096 || ldo > (1 << 23))
+    return MOE_FP4_ERR_UNSUPPORTED;
   if (m_total == 0) return MOE_FP4_OK;
   const GemmTile t = moe_fp4::choose_tile(num_experts, m_total, n, k, getenv("MOE_FP4_TILE"));
   GemmArgs p;

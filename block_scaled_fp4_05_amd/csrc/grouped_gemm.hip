@@ -41,6 +41,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #include "fp4_device.h"
 #include "launch.h"
 
@@ -48,162 +52,263 @@ namespace moe_fp4 {
 namespace {
 
 constexpr int kXcds = 8;
+// Word 3 of a raw buffer resource on gfx9-class GPUs: 32-bit data format,
+// no swizzle, range checking on (an access at or past num_records reads 0 and
+// a store there is dropped).
+constexpr int kRawBufferWord3 = 0x00020000;
+// A buffer offset past every resource built here (each covers < 2^31 bytes).
+constexpr uint32_t kOutOfRange = 0x80000000u;
 
-__device__ __forceinline__ int64_t clamp_off(int32_t v, int64_t m_total) {
-  int64_t x = v;
-  return x < 0 ? 0 : (x > m_total ? m_total : x);
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// Pointers the compiler reads through the scalar cache (uniform addresses).
+typedef const int32_t __attribute__((address_space(4)))* sconst_i32;
+typedef const float __attribute__((address_space(4)))* sconst_f32;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kRawBufferWord3);
 }
 
-// Register image of one K-step for one wavefront: per 16-row block, 32 code
-// bytes and 4 scale bytes per lane.
-template <int MB, int NBW>
+__device__ __forceinline__ int32_t uniform(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// v_writelane_b32: lane J of `v` takes the wavefront-uniform value `s`.
+template <int J>
+__device__ __forceinline__ int32_t write_lane(int32_t v, int32_t s) {
+  asm("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(s), "n"(J));
+  return v;
+}
+
+template <int J>
+__device__ __forceinline__ int32_t gather16(int32_t v, const int32_t (&s)[16]) {
+  if constexpr (J < 16) return gather16<J + 1>(write_lane<J>(v, s[J]), s);
+  else return v;
+}
+
+__device__ __forceinline__ int32_t clamp_off(int32_t v, int32_t m_total) {
+  return v < 0 ? 0 : (v > m_total ? m_total : v);
+}
+
+// Logical number of workgroup b in a grid of nblk (a multiple of 8) when only
+// the first `active` logical workgroups have work: those are split evenly over
+// the 8 XCDs (workgroup b runs on XCD b % 8), consecutive logical numbers on
+// one XCD; the rest follow.  A bijection of [0, nblk).
+__device__ __forceinline__ int logical_block(int b, int nblk, int active) {
+  const int per_xcd = nblk / kXcds;
+  int pxa = (active + kXcds - 1) / kXcds;
+  pxa = pxa < per_xcd ? pxa : per_xcd;
+  const int xcd = b % kXcds, slot = b / kXcds;
+  if (slot < pxa) return xcd * pxa + slot;
+  return kXcds * pxa + xcd * (per_xcd - pxa) + (slot - pxa);
+}
+
+// Register image of one pipeline stage (KSUB sub-steps of 256 K elements) for
+// one wavefront: per 16-row block and sub-step, 32 code bytes and 4 scale
+// bytes per lane.
+template <int MB, int NBW, int KSUB>
 struct Stage {
-  u32x4_t w[NBW][2];
-  uint32_t ws[NBW];
-  u32x4_t a[MB][2];
-  uint32_t as[MB];
+  u32x4_t w[NBW][KSUB][2];
+  uint32_t ws[NBW][KSUB];
+  u32x4_t a[MB][KSUB][2];
+  uint32_t as[MB][KSUB];
 };
 
-// Where a wavefront's current item lives.
-struct Item {
+// Where a work item lives; every field is wavefront-uniform.
+struct ItemPos {
   int32_t e;
   int32_t rows_valid;  // rows of this M-tile that belong to the expert (1..16*MB)
-  int64_t row0;        // first output row of the M-tile
+  int32_t row0;        // first output row of the M-tile
   int32_t n0;          // first output column of the N-tile
+  float alpha;         // a_scale * w_scale[e]
 };
 
+// The loads of a work item: this expert's weight resources and each lane's
+// byte offsets into them and into the activations.
 template <int MB, int NBW>
-__device__ __forceinline__ Item decode_item(int32_t i, const int32_t* prefix, const GemmArgs& p) {
+struct ItemLoads {
+  rsrc_t w, ws;
+  uint32_t w_voff[NBW], ws_voff[NBW];  // lane's weight row, or out of range past n
+  uint32_t a_voff[MB], as_voff[MB];    // lane's (gathered, clamped) activation row
+};
+
+// An empty use of the lane offsets: keeps their registers allocated until the
+// loads that read them have completed (it is placed after the wait for those
+// loads), so decoding the next item never overwrites an address operand of a
+// load still in flight and needs no wait of its own.
+template <int MB, int NBW>
+__device__ __forceinline__ void hold(const ItemLoads<MB, NBW>& l) {
+#pragma unroll
+  for (int jb = 0; jb < NBW; ++jb) asm volatile("" ::"v"(l.w_voff[jb]), "v"(l.ws_voff[jb]));
+#pragma unroll
+  for (int ib = 0; ib < MB; ++ib) asm volatile("" ::"v"(l.a_voff[ib]), "v"(l.as_voff[ib]));
+}
+
+// Item i of the work list: the expert owning it is found by binary search in
+// the LDS prefix of item counts; offsets, the row index and the scales are
+// read through the scalar cache, so decoding issues no vector memory access
+// (the vector-memory counter then only tracks the operand stream).
+template <int MB, int NBW>
+__device__ __forceinline__ void decode_item(int32_t i, const int32_t* prefix, const GemmArgs& p,
+                                            int lane, ItemPos& it, ItemLoads<MB, NBW>& ld) {
   constexpr int BM = 16 * MB;
+  const int c = lane & 15, g = lane >> 4;
   int lo = 0, hi = p.num_experts;  // prefix[lo] <= i < prefix[hi]
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (prefix[mid] <= i) lo = mid; else hi = mid;
   }
-  const int64_t r_lo = clamp_off(p.offsets[lo], p.m_total);
-  const int64_t r_hi = clamp_off(p.offsets[lo + 1], p.m_total);
-  const int32_t cnt = (int32_t)(r_hi - r_lo);
+  lo = uniform(lo);
+  const int32_t m_total = (int32_t)p.m_total;
+  const sconst_i32 offs = (sconst_i32)p.offsets;
+  const int32_t r_lo = clamp_off(offs[lo], m_total);
+  const int32_t r_hi = clamp_off(offs[lo + 1], m_total);
+  const int32_t cnt = r_hi - r_lo;
   const int32_t mts = (cnt + BM - 1) / BM;
-  const int32_t local = i - prefix[lo];
+  const int32_t local = i - uniform(prefix[lo]);
   const int32_t nt = local / mts, mt = local - nt * mts;
-  Item it;
   it.e = lo;
-  it.row0 = r_lo + (int64_t)mt * BM;
+  it.row0 = r_lo + mt * BM;
   const int32_t left = cnt - mt * BM;
   it.rows_valid = left < BM ? left : BM;
   it.n0 = nt * 16 * NBW;
-  return it;
-}
+  it.alpha = ((sconst_f32)p.a_scale)[0] * ((sconst_f32)p.w_scale)[lo];
 
-// Source activation row (gathered, clamped) of each 16-row block for this lane.
-template <int MB>
-__device__ __forceinline__ void source_rows(const Item& it, int c, const GemmArgs& p,
-                                            int64_t (&src)[MB]) {
-#pragma unroll
-  for (int ib = 0; ib < MB; ++ib) {
-    const int rr = 16 * ib + c;
-    const int64_t r = it.row0 + (rr < it.rows_valid ? rr : 0);
-    int64_t s = p.a_row_index ? (int64_t)p.a_row_index[r] : r;
-    s = s < 0 ? 0 : (s >= p.a_rows ? p.a_rows - 1 : s);
-    src[ib] = s;
-  }
-}
-
-template <int MB, int NBW>
-__device__ __forceinline__ void issue_loads(Stage<MB, NBW>& st, const Item& it,
-                                            const int64_t (&src)[MB], int ks, int c, int g,
-                                            const GemmArgs& p) {
-  const int64_t kb = p.k >> 1, nbk = p.k >> 4;
-  const int64_t qoff = (int64_t)ks * 128 + 32 * g;
-  const int64_t soff = (int64_t)ks * 16 + 4 * g;
+  // 32-bit offsets: the host guarantees n * k/2 and a_rows * k/2 < 2^31.
+  const int32_t n = (int32_t)p.n, kb = (int32_t)(p.k >> 1), nbk = (int32_t)(p.k >> 4);
+  ld.w = make_rsrc(p.w_q + (int64_t)lo * n * kb, (uint32_t)(n * kb));
+  ld.ws = make_rsrc(p.w_sf + (int64_t)lo * n * nbk, (uint32_t)(n * nbk));
 #pragma unroll
   for (int jb = 0; jb < NBW; ++jb) {
-    if (it.n0 + 16 * jb < p.n) {
-      const int64_t wrow = (int64_t)it.e * p.n + it.n0 + 16 * jb + c;
-      const uint8_t* wq = p.w_q + wrow * kb + qoff;
-      st.w[jb][0] = load_16B(wq);
-      st.w[jb][1] = load_16B(wq + 16);
-      st.ws[jb] = load_4B(p.w_sf + wrow * nbk + soff);
-    }
+    const int32_t row = it.n0 + 16 * jb + c;
+    const bool ok = row < n;
+    ld.w_voff[jb] = ok ? (uint32_t)(row * kb + 32 * g) : kOutOfRange;
+    ld.ws_voff[jb] = ok ? (uint32_t)(row * nbk + 4 * g) : kOutOfRange;
   }
+  const sconst_i32 idx = (sconst_i32)p.a_row_index;
+  const int32_t a_last = (int32_t)p.a_rows - 1;
 #pragma unroll
   for (int ib = 0; ib < MB; ++ib) {
-    if (16 * ib < it.rows_valid) {
-      const uint8_t* aq = p.a_q + src[ib] * kb + qoff;
-      st.a[ib][0] = load_16B(aq);
-      st.a[ib][1] = load_16B(aq + 16);
-      st.as[ib] = load_4B(p.a_sf + src[ib] * nbk + soff);
+    // Source row of tile row 16*ib + c.  Rows past the expert's end repeat its
+    // first row: their products are computed and never stored.  The 16 row
+    // numbers are read as scalars, written into lanes 0..15, then spread to
+    // every 16-lane group.
+    int32_t src[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int32_t rr = 16 * ib + j;
+      const int32_t r = it.row0 + (rr < it.rows_valid ? rr : 0);
+      src[j] = uniform(idx ? idx[r] : r);
     }
+    int32_t mine = gather16<0>(0, src);
+    mine = __builtin_amdgcn_ds_bpermute(c << 2, mine);
+    mine = mine < 0 ? 0 : (mine > a_last ? a_last : mine);
+    ld.a_voff[ib] = (uint32_t)(mine * kb + 32 * g);
+    ld.as_voff[ib] = (uint32_t)(mine * nbk + 4 * g);
   }
 }
 
-template <int MB, int NBW>
-__device__ __forceinline__ void compute_stage(const Stage<MB, NBW>& st, const Item& it,
-                                              const GemmArgs& p, float4_t (&acc)[NBW][MB]) {
-  // Block scales of this step, as FP16 value * 2^-8: scale t/2 serves MFMA t.
-  half2_t wsc[NBW][2], asc[MB][2];
+// Issue every load of one stage: K sub-steps kss .. kss+KSUB-1 (256 elements
+// each).  Unconditional, so the compiler can count outstanding loads exactly;
+// weight rows past n read zeros.  The per-lane offsets stay fixed for a whole
+// item and the K position goes in the scalar offset, so the loop writes no
+// VGPR that an in-flight load still reads.
+template <int MB, int NBW, int KSUB>
+__device__ __forceinline__ void issue_loads(Stage<MB, NBW, KSUB>& st, const ItemLoads<MB, NBW>& it,
+                                            const rsrc_t& a_rs, const rsrc_t& as_rs, int32_t kss) {
 #pragma unroll
-  for (int jb = 0; jb < NBW; ++jb) {
-    wsc[jb][0] = scale_pair_x2m8<false>(st.ws[jb]);
-    wsc[jb][1] = scale_pair_x2m8<true>(st.ws[jb]);
-  }
-#pragma unroll
-  for (int ib = 0; ib < MB; ++ib) {
-    asc[ib][0] = scale_pair_x2m8<false>(st.as[ib]);
-    asc[ib][1] = scale_pair_x2m8<true>(st.as[ib]);
-  }
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const int half = t >> 2, word = t & 3, sidx = (t >> 1) & 1, spair = t >> 2;
-    half8_t af[MB];
-#pragma unroll
-    for (int ib = 0; ib < MB; ++ib) {
-      if (16 * ib < it.rows_valid) af[ib] = dequant8(st.a[ib][half][word], asc[ib][spair][sidx]);
-    }
+  for (int s = 0; s < KSUB; ++s) {
+    const int32_t qk = uniform((kss + s) * 128), sk = uniform((kss + s) * 16);
 #pragma unroll
     for (int jb = 0; jb < NBW; ++jb) {
-      if (it.n0 + 16 * jb < p.n) {
-        const half8_t wf = dequant8(st.w[jb][half][word], wsc[jb][spair][sidx]);
+      st.w[jb][s][0] = __builtin_amdgcn_raw_buffer_load_b128(it.w, it.w_voff[jb], qk, 0);
+      st.w[jb][s][1] = __builtin_amdgcn_raw_buffer_load_b128(it.w, it.w_voff[jb] + 16u, qk, 0);
+      st.ws[jb][s] = __builtin_amdgcn_raw_buffer_load_b32(it.ws, it.ws_voff[jb], sk, 0);
+    }
 #pragma unroll
-        for (int ib = 0; ib < MB; ++ib) {
-          if (16 * ib < it.rows_valid)
-            acc[jb][ib] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf, af[ib], acc[jb][ib], 0, 0, 0);
+    for (int ib = 0; ib < MB; ++ib) {
+      st.a[ib][s][0] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, it.a_voff[ib], qk, 0);
+      st.a[ib][s][1] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, it.a_voff[ib] + 16u, qk, 0);
+      st.as[ib][s] = __builtin_amdgcn_raw_buffer_load_b32(as_rs, it.as_voff[ib], sk, 0);
+    }
+  }
+}
+
+template <int MB, int NBW, int KSUB>
+__device__ __forceinline__ void compute_stage(const Stage<MB, NBW, KSUB>& st,
+                                              const ItemPos& it, int32_t n,
+                                              float4_t (&acc)[NBW][MB]) {
+#pragma unroll
+  for (int s = 0; s < KSUB; ++s) {
+    // Block scales of this sub-step, as FP16 value * 2^-8: scale t/2 serves MFMA t.
+    half2_t wsc[NBW][2], asc[MB][2];
+#pragma unroll
+    for (int jb = 0; jb < NBW; ++jb) {
+      wsc[jb][0] = scale_pair_x2m8<false>(st.ws[jb][s]);
+      wsc[jb][1] = scale_pair_x2m8<true>(st.ws[jb][s]);
+    }
+#pragma unroll
+    for (int ib = 0; ib < MB; ++ib) {
+      asc[ib][0] = scale_pair_x2m8<false>(st.as[ib][s]);
+      asc[ib][1] = scale_pair_x2m8<true>(st.as[ib][s]);
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int half = t >> 2, word = t & 3, sidx = (t >> 1) & 1, spair = t >> 2;
+      half8_t af[MB];
+#pragma unroll
+      for (int ib = 0; ib < MB; ++ib)
+        af[ib] = dequant8(st.a[ib][s][half][word], asc[ib][spair][sidx]);
+#pragma unroll
+      for (int jb = 0; jb < NBW; ++jb) {
+        if (it.n0 + 16 * jb < n) {  // uniform: skip column blocks past n
+          const half8_t wf = dequant8(st.w[jb][s][half][word], wsc[jb][spair][sidx]);
+#pragma unroll
+          for (int ib = 0; ib < MB; ++ib) {
+            if (16 * ib < it.rows_valid)  // uniform: skip row blocks past the expert
+              acc[jb][ib] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf, af[ib], acc[jb][ib], 0, 0, 0);
+          }
         }
       }
     }
   }
 }
 
+// BF16 store of a finished item.  Lane (c, g) holds rows 16*ib + c, columns
+// 16*jb + 4g .. +3.  Stores go through a buffer resource covering exactly the
+// item's valid rows, so rows past the expert's end fall outside it and are
+// dropped; column blocks past n get an out-of-range offset.  No branches.
 template <int MB, int NBW>
-__device__ __forceinline__ void epilogue(float4_t (&acc)[NBW][MB], const Item& it, int c, int g,
-                                         const GemmArgs& p) {
-  const float alpha = p.a_scale[0] * p.w_scale[it.e];
+__device__ __forceinline__ void epilogue(float4_t (&acc)[NBW][MB], const ItemPos& it,
+                                         int c, int g, const GemmArgs& p) {
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  const rsrc_t o = make_rsrc(p.out + (int64_t)it.row0 * p.ldo,
+                             (uint32_t)((int64_t)it.rows_valid * p.ldo * 2));
 #pragma unroll
   for (int jb = 0; jb < NBW; ++jb) {
 #pragma unroll
     for (int ib = 0; ib < MB; ++ib) {
-      const int rr = 16 * ib + c;
-      if (it.n0 + 16 * jb < p.n && rr < it.rows_valid) {
-        typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-        const float4_t v = acc[jb][ib];
-        const bf16x4_t b = {(__bf16)(v[0] * alpha), (__bf16)(v[1] * alpha),
-                            (__bf16)(v[2] * alpha), (__bf16)(v[3] * alpha)};
-        uint16_t* o = p.out + (it.row0 + rr) * p.ldo + it.n0 + 16 * jb + 4 * g;
-        *reinterpret_cast<u32x2_t*>(o) = __builtin_bit_cast(u32x2_t, b);
-      }
+      const float4_t v = acc[jb][ib];
+      const bf16x4_t b = {(__bf16)(v[0] * it.alpha), (__bf16)(v[1] * it.alpha),
+                          (__bf16)(v[2] * it.alpha), (__bf16)(v[3] * it.alpha)};
+      const int32_t col = it.n0 + 16 * jb;
+      const uint32_t off = col < (int32_t)p.n
+          ? (uint32_t)(((16 * ib + c) * (int32_t)p.ldo + col + 4 * g) * 2)
+          : kOutOfRange;
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, b), o, off, 0, 0);
       acc[jb][ib] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
   }
 }
 
-template <int MB, int NBW, int WAVES>
+template <int MB, int NBW, int KSUB, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void k_grouped_gemm(const GemmArgs p) {
   constexpr int BM = 16 * MB;
   constexpr int NTHR = WAVES * 64;
   extern __shared__ int32_t prefix[];  // [num_experts + 1] item prefix
   __shared__ int32_t wave_sum[WAVES];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6);  // the compiler cannot see that this is wave-uniform
   const int E = p.num_experts;
+  const int32_t m_total = (int32_t)p.m_total;
 
   // ---- work list: exclusive prefix over experts of (M-tiles * N-tiles) ----
   {
@@ -212,8 +317,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_grouped_gemm(const GemmArgs p) {
     const int end = beg + per < E ? beg + per : E;
     int32_t local = 0;
     for (int e = beg; e < end; ++e) {
-      const int64_t cnt = clamp_off(p.offsets[e + 1], p.m_total) - clamp_off(p.offsets[e], p.m_total);
-      local += cnt > 0 ? (int32_t)((cnt + BM - 1) / BM) * p.n_tiles : 0;
+      const int32_t cnt = clamp_off(p.offsets[e + 1], m_total) - clamp_off(p.offsets[e], m_total);
+      local += cnt > 0 ? ((cnt + BM - 1) / BM) * p.n_tiles : 0;
     }
     int32_t incl = local;
 #pragma unroll
@@ -228,27 +333,40 @@ __global__ __launch_bounds__(WAVES * 64) void k_grouped_gemm(const GemmArgs p) {
     int32_t run = base + incl - local;
     for (int e = beg; e < end; ++e) {
       prefix[e] = run;
-      const int64_t cnt = clamp_off(p.offsets[e + 1], p.m_total) - clamp_off(p.offsets[e], p.m_total);
-      run += cnt > 0 ? (int32_t)((cnt + BM - 1) / BM) * p.n_tiles : 0;
+      const int32_t cnt = clamp_off(p.offsets[e + 1], m_total) - clamp_off(p.offsets[e], m_total);
+      run += cnt > 0 ? ((cnt + BM - 1) / BM) * p.n_tiles : 0;
     }
     if (tid == NTHR - 1) prefix[E] = base + incl;
     __syncthreads();
   }
-  const int32_t total_items = prefix[E];
+  const int32_t total_items = uniform(prefix[E]);
 
   // ---- XCD-aware wavefront numbering ----
+  // Items are dealt in rounds of nw (one per wavefront).  Within a round, the
+  // active workgroups (those whose waves have an item) are spread evenly over
+  // the 8 XCDs, and consecutive items go to consecutive waves of one XCD.  The
+  // hardware places workgroup b on XCD b % 8; the grid is a multiple of 8.
   const int nblk = gridDim.x, b = blockIdx.x;
-  const int xcd = b % kXcds, slot = b / kXcds;
-  const int per_xcd = nblk / kXcds, rem = nblk % kXcds;
-  const int lblk = xcd * per_xcd + (xcd < rem ? xcd : rem) + slot;
-  const int32_t lw = lblk * WAVES + wave;
   const int32_t nw = nblk * WAVES;
-  if (lw >= total_items) return;
+  const int32_t rounds = (total_items + nw - 1) / nw;
+  if (rounds == 0) return;
+  const int32_t last_items = total_items - (rounds - 1) * nw;
+  const int32_t lw_full = logical_block(b, nblk, nblk) * WAVES + wave;
+  const int32_t lw_last =
+      logical_block(b, nblk, (last_items + WAVES - 1) / WAVES) * WAVES + wave;
+  const int32_t my_items = (rounds - 1) + (lw_last < last_items ? 1 : 0);
+  if (my_items == 0) return;
+  auto item_of = [&](int32_t j) -> int32_t {
+    return j * nw + (j == rounds - 1 ? lw_last : lw_full);
+  };
 
   const int c = lane & 15, g = lane >> 4;
-  const int nks = (int)(p.k / kKStep);
-  const int32_t my_items = (total_items - lw + nw - 1) / nw;
-  const int64_t units = (int64_t)my_items * nks;
+  const int32_t nsub = (int32_t)(p.k / 256);    // 256-element sub-steps per row
+  const int32_t nst = nsub / KSUB;              // stages per item
+  const int32_t units = my_items * nst;  // < 2^31 (host bound on items * stages)
+  const rsrc_t a_rs = make_rsrc(p.a_q, (uint32_t)(p.a_rows * (p.k >> 1)));
+  const rsrc_t as_rs = make_rsrc(p.a_sf, (uint32_t)(p.a_rows * (p.k >> 4)));
+  const int32_t n = (int32_t)p.n;
 
   float4_t acc[NBW][MB];
 #pragma unroll
@@ -256,77 +374,112 @@ __global__ __launch_bounds__(WAVES * 64) void k_grouped_gemm(const GemmArgs p) {
 #pragma unroll
     for (int ib = 0; ib < MB; ++ib) acc[jb][ib] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  Stage<MB, NBW> s0, s1;
-  // Item of the unit being loaded (ld_*) and of the unit being computed (cp_*).
-  int32_t ld_item = lw;
-  int ld_ks = 0;
-  Item ld_it = decode_item<MB, NBW>(ld_item, prefix, p);
-  int64_t ld_src[MB];
-  source_rows<MB>(ld_it, c, p, ld_src);
-  Item cp_it = ld_it;
-
-  auto advance = [&]() {
-    if (++ld_ks == nks) {
-      ld_ks = 0;
-      ld_item += nw;
-      ld_it = decode_item<MB, NBW>(ld_item, prefix, p);
-      source_rows<MB>(ld_it, c, p, ld_src);
+  // ld_*: the unit whose loads are issued next; cp: the item being accumulated.
+  // Each register stage has its own set of lane offsets (l0 for s0, l1 for s1).
+  ItemPos ld_pos, cp;
+  ItemLoads<MB, NBW> l0, l1;
+  int32_t ld_round = 0, ld_st = 0, cp_st = 0;
+  decode_item<MB, NBW>(item_of(0), prefix, p, lane, ld_pos, l0);
+  cp = ld_pos;
+  // Move the load position to the next unit: a new item is decoded into dst,
+  // otherwise dst takes src's offsets.
+  auto advance = [&](ItemLoads<MB, NBW>& dst, const ItemLoads<MB, NBW>& src) {
+    if (++ld_st == nst) {
+      ld_st = 0;
+      ++ld_round;
+      decode_item<MB, NBW>(item_of(ld_round), prefix, p, lane, ld_pos, dst);
+    } else {
+      dst = src;
+    }
+  };
+  auto retire = [&]() {
+    if (++cp_st == nst) {
+      epilogue<MB, NBW>(acc, cp, c, g, p);
+      cp_st = 0;
+      cp = ld_pos;
     }
   };
 
-  issue_loads<MB, NBW>(s0, ld_it, ld_src, ld_ks, c, g, p);
-  int cp_ks = 0;
-  for (int64_t u = 0; u < units; u += 2) {
-    // even unit: prefetch u+1 into s1, compute s0
-    const bool has1 = u + 1 < units;
-    if (has1) {
-      advance();
-      issue_loads<MB, NBW>(s1, ld_it, ld_src, ld_ks, c, g, p);
-    }
-    compute_stage<MB, NBW>(s0, cp_it, p, acc);
-    if (++cp_ks == nks) {
-      epilogue<MB, NBW>(acc, cp_it, c, g, p);
-      cp_ks = 0;
-      if (has1) cp_it = ld_it;
-    }
-    if (!has1) break;
-    // odd unit: prefetch u+2 into s0, compute s1
-    const bool has2 = u + 2 < units;
-    if (has2) {
-      advance();
-      issue_loads<MB, NBW>(s0, ld_it, ld_src, ld_ks, c, g, p);
-    }
-    compute_stage<MB, NBW>(s1, cp_it, p, acc);
-    if (++cp_ks == nks) {
-      epilogue<MB, NBW>(acc, cp_it, c, g, p);
-      cp_ks = 0;
-      if (has2) cp_it = ld_it;
-    }
+  // Two register stages.  Every iteration issues the next stage's loads (at
+  // the very end it re-reads the last stage, which the caches serve) before
+  // computing the current one, so one stage is always in flight.
+  Stage<MB, NBW, KSUB> s0, s1;
+  issue_loads<MB, NBW, KSUB>(s0, l0, a_rs, as_rs, ld_st * KSUB);
+  for (int32_t u = 0;; u += 2) {
+    const bool more1 = u + 1 < units;
+    if (more1) advance(l1, l0); else l1 = l0;
+    issue_loads<MB, NBW, KSUB>(s1, l1, a_rs, as_rs, ld_st * KSUB);
+    compute_stage<MB, NBW, KSUB>(s0, cp, n, acc);
+    hold<MB, NBW>(l0);
+    retire();
+    if (!more1) break;
+    const bool more2 = u + 2 < units;
+    if (more2) advance(l0, l1); else l0 = l1;
+    issue_loads<MB, NBW, KSUB>(s0, l0, a_rs, as_rs, ld_st * KSUB);
+    compute_stage<MB, NBW, KSUB>(s1, cp, n, acc);
+    hold<MB, NBW>(l1);
+    retire();
+    if (!more2) break;
   }
 }
 
-template <int MB, int NBW, int WAVES>
-hipError_t launch_tile(const GemmArgs& p, hipStream_t stream) {
-  auto kern = k_grouped_gemm<MB, NBW, WAVES>;
-  const size_t lds = sizeof(int32_t) * ((size_t)p.num_experts + 1);
+// Resident workgroups the device can hold for one kernel, queried once per
+// (device, kernel, LDS size) and kept: the query costs more host time than a
+// small decode GEMM takes on the GPU.
+struct ResidentCache {
+  std::mutex mu;
+  std::map<std::tuple<int, const void*, size_t>, int> groups;
+};
+
+inline ResidentCache& resident_cache() {
+  static ResidentCache c;
+  return c;
+}
+
+template <typename K>
+hipError_t resident_groups(K kern, int threads, size_t lds, int* out) {
   int dev = 0;
   hipError_t err = hipGetDevice(&dev);
   if (err != hipSuccess) return err;
+  const auto key = std::make_tuple(dev, reinterpret_cast<const void*>(kern), lds);
+  ResidentCache& c = resident_cache();
+  {
+    std::lock_guard<std::mutex> g(c.mu);
+    auto it = c.groups.find(key);
+    if (it != c.groups.end()) {
+      *out = it->second;
+      return hipSuccess;
+    }
+  }
   int cus = 0;
   err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (err != hipSuccess) return err;
   int per_cu = 0;
-  err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, WAVES * 64, lds);
+  err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, lds);
   if (err != hipSuccess) return err;
   if (per_cu < 1) per_cu = 1;
+  std::lock_guard<std::mutex> g(c.mu);
+  c.groups[key] = cus * per_cu;
+  *out = cus * per_cu;
+  return hipSuccess;
+}
+
+template <int MB, int NBW, int KSUB, int WAVES>
+hipError_t launch_tile(const GemmArgs& p, hipStream_t stream) {
+  auto kern = k_grouped_gemm<MB, NBW, KSUB, WAVES>;
+  const size_t lds = sizeof(int32_t) * ((size_t)p.num_experts + 1);
+  int resident = 0;
+  hipError_t err = resident_groups(kern, WAVES * 64, lds, &resident);
+  if (err != hipSuccess) return err;
   // Upper bound on the number of items: the host does not see the offsets.
   constexpr int BM = 16 * MB;
   const int64_t max_mtiles = p.m_total / BM + (p.m_total < p.num_experts ? p.m_total : p.num_experts);
   const int64_t max_items = max_mtiles * p.n_tiles;
-  int64_t grid = (int64_t)cus * per_cu;
+  int64_t grid = resident;
   const int64_t need = (max_items + WAVES - 1) / WAVES;
   if (need < grid) grid = need;
   if (grid < 1) grid = 1;
+  grid = (grid + kXcds - 1) / kXcds * kXcds;  // whole rounds over the XCDs
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WAVES * 64), lds, stream, p);
   return hipGetLastError();
 }
@@ -335,22 +488,31 @@ hipError_t launch_tile(const GemmArgs& p, hipStream_t stream) {
 
 GemmTile choose_tile(int32_t num_experts, int64_t m_total, int64_t n, int64_t k, const char* env) {
   (void)n;
-  (void)k;
-  GemmTile t{1, 4, 4};
+  GemmTile t{1, 4, 4, 1};
   const int64_t avg = num_experts > 0 ? (m_total + num_experts - 1) / num_experts : m_total;
   if (avg > 32) t.m_blocks = 4;
   else if (avg > 16) t.m_blocks = 2;
+  if (k % 512 == 0) t.k_sub = 2;
   if (env && *env) {
-    int bm = 0, bn = 0;
+    // "MxN" or "MxNxK": M rows per item, N columns per wave, K elements per stage.
+    int v[3] = {0, 0, 0};
+    int nv = 0;
     const char* s = env;
-    while (*s >= '0' && *s <= '9') bm = bm * 10 + (*s++ - '0');
-    if (*s == 'x' || *s == 'X') {
-      ++s;
-      while (*s >= '0' && *s <= '9') bn = bn * 10 + (*s++ - '0');
-      if ((bm == 16 || bm == 32 || bm == 64) && (bn == 32 || bn == 64) && *s == '\0') {
-        t.m_blocks = bm / 16;
-        t.n_blocks = bn / 16;
-      }
+    bool ok = true;
+    while (ok && nv < 3) {
+      if (*s < '0' || *s > '9') { ok = false; break; }
+      while (*s >= '0' && *s <= '9') v[nv] = v[nv] * 10 + (*s++ - '0');
+      ++nv;
+      if (*s == '\0') break;
+      if (*s == 'x' || *s == 'X') ++s; else ok = false;
+    }
+    ok = ok && *s == '\0' && nv >= 2;
+    ok = ok && (v[0] == 16 || v[0] == 32 || v[0] == 64) && (v[1] == 32 || v[1] == 64);
+    if (nv == 3) ok = ok && (v[2] == 256 || (v[2] == 512 && k % 512 == 0));
+    if (ok) {
+      t.m_blocks = v[0] / 16;
+      t.n_blocks = v[1] / 16;
+      if (nv == 3) t.k_sub = v[2] / 256;
     }
   }
   return t;
@@ -360,22 +522,25 @@ int64_t gemm_lds_bytes(const GemmTile& t, int32_t num_experts) {
   return (int64_t)sizeof(int32_t) * ((int64_t)num_experts + 1 + t.waves);
 }
 
+template <int NBW, int KSUB>
+hipError_t launch_mb(const GemmArgs& p, int m_blocks, hipStream_t stream) {
+  switch (m_blocks) {
+    case 1: return launch_tile<1, NBW, KSUB, 4>(p, stream);
+    case 2: return launch_tile<2, NBW, KSUB, 4>(p, stream);
+    case 4: return launch_tile<4, NBW, KSUB, 4>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_grouped_gemm(const GemmArgs& p, const GemmTile& t, hipStream_t stream) {
-  if (t.waves != 4) return hipErrorInvalidValue;
+  if (t.waves != 4 || p.k % (256 * t.k_sub) != 0) return hipErrorInvalidValue;
   if (t.n_blocks == 4) {
-    switch (t.m_blocks) {
-      case 1: return launch_tile<1, 4, 4>(p, stream);
-      case 2: return launch_tile<2, 4, 4>(p, stream);
-      case 4: return launch_tile<4, 4, 4>(p, stream);
-      default: break;
-    }
-  } else if (t.n_blocks == 2) {
-    switch (t.m_blocks) {
-      case 1: return launch_tile<1, 2, 4>(p, stream);
-      case 2: return launch_tile<2, 2, 4>(p, stream);
-      case 4: return launch_tile<4, 2, 4>(p, stream);
-      default: break;
-    }
+    return t.k_sub == 2 ? launch_mb<4, 2>(p, t.m_blocks, stream)
+                        : launch_mb<4, 1>(p, t.m_blocks, stream);
+  }
+  if (t.n_blocks == 2) {
+    return t.k_sub == 2 ? launch_mb<2, 2>(p, t.m_blocks, stream)
+                        : launch_mb<2, 1>(p, t.m_blocks, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -14,17 +14,20 @@ hipError_t launch_quantize(const void* x, int in_dtype, int64_t rows, int64_t k,
 
 // Tile shapes of the grouped GEMM.  Rows per work item = 16 * m_blocks; output
 // columns per wavefront = 16 * n_blocks; a workgroup holds `waves` wavefronts,
-// each working on its own item.
+// each working on its own item; one pipeline stage covers 256 * k_sub
+// elements of K.
 struct GemmTile {
   int m_blocks;
   int n_blocks;
   int waves;
+  int k_sub;
 };
 
-constexpr int kKStep = 256;  // K elements consumed per main-loop iteration
+constexpr int kKStep = 256;  // K granularity the kernels require
 
 // The tile used for a problem with these sizes; `env` (may be NULL) is the
-// value of MOE_FP4_TILE ("MxN" with M rows per item and N columns per wave).
+// value of MOE_FP4_TILE ("MxN" or "MxNxK": M rows per item, N columns per
+// wave, K elements per pipeline stage).
 GemmTile choose_tile(int32_t num_experts, int64_t m_total, int64_t n, int64_t k, const char* env);
 
 // LDS bytes a workgroup of the grouped GEMM uses for `num_experts` experts.

@@ -7,11 +7,18 @@
 // definition, stated in moe_fp4.h.
 //
 // Kernels, in stream order:
-//   DYNAMIC: reset -> amax -> quantize (derives g from amax) -> finalize (g in place)
-//   STATIC:  quantize (reads g)
-// The amax is accumulated in the caller's tensor_scale float itself (as the bit
-// pattern of a non-negative float, for which unsigned max is float max), so no
-// scratch memory is needed, and the reset is a kernel rather than a memset.
+//   DYNAMIC: reset -> amax -> quantize      STATIC: quantize
+// The dynamic tensor scale is reduced in the caller's tensor_scale float
+// itself, so no scratch memory is needed.  Since g = fl(amax / 2688) is a
+// non-decreasing function of amax, the maximum of the per-workgroup values
+// fl(amax_wg / 2688) is g itself: each workgroup folds its own value in with
+// one integer atomic max on the float's bit pattern (signed order agrees with
+// float order for non-negative floats).  The reset writes -0.0 (bit pattern
+// INT_MIN), below every non-negative pattern, and a workgroup whose elements
+// are all zero contributes nothing, so -0.0 surviving the amax pass means an
+// all-zero tensor, for which g = 1; the quantiser reads it as 1 and writes 1.
+// The reset is a kernel rather than a memset so the sequence can be captured
+// in a graph.
 //
 // One thread quantises one 16-element block: 32 (BF16) or 64 (FP32) bytes in,
 // 8 bytes of codes and 1 scale byte out, consecutive threads on consecutive
@@ -55,13 +62,20 @@ __device__ __forceinline__ void load_block16(const void* x, int64_t row, int64_t
   }
 }
 
+constexpr uint32_t kNoAmax = 0x80000000u;  // -0.0f: "no non-zero element seen"
+
 __global__ void k_amax_reset(float* ts) {
-  if (blockIdx.x == 0 && threadIdx.x == 0) *reinterpret_cast<uint32_t*>(ts) = 0u;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *reinterpret_cast<uint32_t*>(ts) = kNoAmax;
+}
+
+__global__ void k_set_one(float* ts) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *ts = 1.0f;
 }
 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_amax(const void* x, int64_t rows, int64_t k,
                                                    int64_t ld_x, float* ts) {
+  __shared__ float wave_max[kThreads / 64];
   const int64_t nb = k / 16;
   const int64_t total = rows * nb;
   float m = 0.0f;
@@ -74,16 +88,26 @@ __global__ __launch_bounds__(kThreads) void k_amax(const void* x, int64_t rows, 
   }
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
-  if ((threadIdx.x & 63) == 0 && m > 0.0f)
-    atomicMax(reinterpret_cast<uint32_t*>(ts), __builtin_bit_cast(uint32_t, m));
+  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float wg = wave_max[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) wg = fmaxf(wg, wave_max[w]);
+    if (wg > 0.0f) {
+      const float g = wg / 2688.0f;  // IEEE division, rounded to nearest even
+      atomicMax(reinterpret_cast<int*>(ts), __builtin_bit_cast(int, g));
+    }
+  }
 }
 
-// Tensor scale from the accumulated amax (DYNAMIC) or as given (STATIC).
+// Tensor scale: the reduced value (DYNAMIC; -0.0 means all-zero input, g = 1)
+// or the caller's calibrated value (STATIC).
 template <bool DYN>
 __device__ __forceinline__ float tensor_scale_of(const float* ts) {
   const float t = *ts;
   if (!DYN) return t;
-  return t > 0.0f ? t / 2688.0f : 1.0f;
+  return __builtin_bit_cast(uint32_t, t) == kNoAmax ? 1.0f : t;
 }
 
 template <int DT, bool DYN>
@@ -91,6 +115,10 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const void* x, int64_t ro
                                                        int64_t ld_x, uint8_t* q, uint8_t* sf,
                                                        const float* ts) {
   const float g = tensor_scale_of<DYN>(ts);
+  // All-zero input: publish g = 1.  Other workgroups may still read the
+  // sentinel or the 1.0, and both mean 1.
+  if (DYN && blockIdx.x == 0 && threadIdx.x == 0 && g == 1.0f)
+    *const_cast<float*>(ts) = 1.0f;
   const float six_g = 6.0f * g;
   const int64_t nb = k / 16;
   const int64_t total = rows * nb;
@@ -123,9 +151,6 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const void* x, int64_t ro
   }
 }
 
-__global__ void k_amax_finalize(float* ts) {
-  if (blockIdx.x == 0 && threadIdx.x == 0) *ts = tensor_scale_of<true>(ts);
-}
 
 template <int DT>
 hipError_t launch_dt(const void* x, int64_t rows, int64_t k, int64_t ld_x, uint8_t* q, uint8_t* sf,
@@ -134,14 +159,16 @@ hipError_t launch_dt(const void* x, int64_t rows, int64_t k, int64_t ld_x, uint8
   const int64_t want = (total + kThreads - 1) / kThreads;
   const int grid = (int)(want < 65536 ? (want > 0 ? want : 1) : 65536);
   if (dynamic) {
-    hipLaunchKernelGGL(k_amax_reset, dim3(1), dim3(64), 0, stream, ts);
     if (total > 0) {
-      const int agrid = grid < 2048 ? grid : 2048;
+      // Few workgroups with one atomic each: the reduction target is one word.
+      const int agrid = grid < 256 ? grid : 256;
+      hipLaunchKernelGGL(k_amax_reset, dim3(1), dim3(64), 0, stream, ts);
       hipLaunchKernelGGL((k_amax<DT>), dim3(agrid), dim3(kThreads), 0, stream, x, rows, k, ld_x, ts);
       hipLaunchKernelGGL((k_quantize<DT, true>), dim3(grid), dim3(kThreads), 0, stream, x, rows, k,
                          ld_x, q, sf, (const float*)ts);
+    } else {
+      hipLaunchKernelGGL(k_set_one, dim3(1), dim3(64), 0, stream, ts);
     }
-    hipLaunchKernelGGL(k_amax_finalize, dim3(1), dim3(64), 0, stream, ts);
   } else if (total > 0) {
     hipLaunchKernelGGL((k_quantize<DT, false>), dim3(grid), dim3(kThreads), 0, stream, x, rows, k,
                        ld_x, q, sf, (const float*)ts);

@@ -106,11 +106,12 @@ def gemm_raw(*args):
 
 
 def quantize(x: torch.Tensor, tensor_scale: torch.Tensor | None = None, q=None, sf=None,
-             stream=None):
+             stream=None, dynamic: bool | None = None):
     """NVFP4-quantise a 2-D BF16 or FP32 CUDA tensor [rows][k].
 
     tensor_scale None -> dynamic: a new 1-element float32 tensor receives g.
-    Otherwise a 1-element float32 CUDA tensor holding a calibrated g (static).
+    Otherwise a 1-element float32 CUDA tensor: by default it holds a calibrated g
+    (static); with dynamic=True it receives the computed g instead.
     Returns (q uint8[rows][k/2], sf uint8[rows][k/16], tensor_scale float32[1]).
     """
     if x.dim() != 2 or x.stride(1) != 1:
@@ -127,10 +128,13 @@ def quantize(x: torch.Tensor, tensor_scale: torch.Tensor | None = None, q=None, 
         q = torch.empty((rows, k // 2), dtype=torch.uint8, device=dev)
     if sf is None:
         sf = torch.empty((rows, k // 16), dtype=torch.uint8, device=dev)
-    mode = SCALE_STATIC
+    if dynamic is None:
+        dynamic = tensor_scale is None
+    mode = SCALE_DYNAMIC if dynamic else SCALE_STATIC
     if tensor_scale is None:
+        if not dynamic:
+            raise ValueError("a static quantisation needs tensor_scale")
         tensor_scale = torch.empty(1, dtype=torch.float32, device=dev)
-        mode = SCALE_DYNAMIC
     st = lib().moe_fp4_quantize(_ptr(x), dt, rows, k, x.stride(0), _ptr(q), _ptr(sf),
                                 _ptr(tensor_scale), mode, _stream(stream))
     if st != OK:

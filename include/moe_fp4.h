@@ -96,6 +96,8 @@ enum {
  *   scale_mode   MOE_FP4_SCALE_STATIC or MOE_FP4_SCALE_DYNAMIC.
  *   stream       hipStream_t or NULL.
  * Inputs must be finite; the result for NaN or Inf inputs is unspecified.
+ * DYNAMIC mode also needs amax = 0 or fl(amax / 2688) > 0 (amax above about
+ * 2^-138); below that g underflows to 0 and the block scales are undefined.
  * Errors: NULL (x, q, sf or tensor_scale NULL with rows > 0; tensor_scale
  * NULL always), SHAPE (rows < 0, k <= 0, k % 16, ld_x < k), ALIGN, ARG, HIP.
  */

@@ -29,8 +29,12 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#include <omp.h>
 
 #define EXPORT __attribute__((visibility("default")))
+
+/* Threads the OpenMP loops below run on (reported beside oracle timings). */
+EXPORT int oracle_num_threads(void) { return omp_get_max_threads(); }
 
 /* ---------------------------------------------------------------- E2M1 ---- */
 

@@ -55,6 +55,8 @@ def _load():
     c_f32p = ctypes.POINTER(ctypes.c_float)
     c_f64p = ctypes.POINTER(ctypes.c_double)
     c_u16p = ctypes.POINTER(ctypes.c_uint16)
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_e2m1_decode.argtypes = [ctypes.c_int]
     lib.oracle_e2m1_decode.restype = ctypes.c_double
     lib.oracle_e2m1_encode.argtypes = [ctypes.c_float]
@@ -83,6 +85,11 @@ def _ptr(a, ctype):
     if a is None:
         return None
     return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return _load().oracle_num_threads()
 
 
 # ------------------------------------------------------------------ codecs --

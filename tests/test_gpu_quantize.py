@@ -112,6 +112,22 @@ def test_zero_rows_dynamic_scale_is_one():
     assert q.shape == (0, 32) and float(g.cpu()[0]) == 1.0
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_all_zero_tensor_dynamic_scale_is_one(dtype):
+    """Every workgroup sees only zeros: the tensor scale must come out as 1.0 and
+    every code and block scale as 0, as in the oracle."""
+    x = np.zeros((300, 512), np.float32)
+    x[7, 3] = -0.0
+    _check(x, dtype, label="all-zero")
+
+
+def test_single_nonzero_element_sets_the_tensor_scale():
+    """One non-zero element far from workgroup 0: its workgroup alone sets g."""
+    x = np.zeros((300, 512), np.float32)
+    x[297, 500] = -3.75
+    _check(x, torch.float32, label="single nonzero")
+
+
 def test_deterministic_and_stream_safe():
     from block_scaled_fp4_05_amd import moe_fp4
     x = dev(gen.bf16_round(gen.normal((512, 6144), 41))).to(torch.bfloat16)
