@@ -102,8 +102,12 @@ __device__ __forceinline__ int logical_block(int b, int nblk, int active) {
 }
 
 // Register image of one pipeline stage (KSUB sub-steps of 256 K elements) for
-// one wavefront: per 16-row block and sub-step, 32 code bytes and 4 scale
-// bytes per lane.
+// one wavefront.  Within a stage, lane group g (lanes 16g .. 16g+15, one row
+// each) owns the contiguous K run [64*KSUB*g, 64*KSUB*(g+1)) of the stage: per
+// 16-row block and sub-step s, 32 code bytes (elements 64s .. 64s+63 of its
+// run) and one scale dword; the KSUB scale dwords of a lane are adjacent in
+// memory and arrive in one load.  Weights and activations use the same K
+// order, so every product pairs the same K element.
 template <int MB, int NBW, int KSUB>
 struct Stage {
   u32x4_t w[NBW][KSUB][2];
@@ -142,11 +146,23 @@ __device__ __forceinline__ void hold(const ItemLoads<MB, NBW>& l) {
   for (int ib = 0; ib < MB; ++ib) asm volatile("" ::"v"(l.a_voff[ib]), "v"(l.as_voff[ib]));
 }
 
+// The same loads with every offset out of range: they return zeros without a
+// memory request (used for the one surplus issue at the end of a wave's work).
+template <int MB, int NBW>
+__device__ __forceinline__ ItemLoads<MB, NBW> nowhere(const ItemLoads<MB, NBW>& l) {
+  ItemLoads<MB, NBW> z = l;
+#pragma unroll
+  for (int jb = 0; jb < NBW; ++jb) z.w_voff[jb] = z.ws_voff[jb] = kOutOfRange;
+#pragma unroll
+  for (int ib = 0; ib < MB; ++ib) z.a_voff[ib] = z.as_voff[ib] = kOutOfRange;
+  return z;
+}
+
 // Item i of the work list: the expert owning it is found by binary search in
 // the LDS prefix of item counts; offsets, the row index and the scales are
 // read through the scalar cache, so decoding issues no vector memory access
 // (the vector-memory counter then only tracks the operand stream).
-template <int MB, int NBW>
+template <int MB, int NBW, int KSUB>
 __device__ __forceinline__ void decode_item(int32_t i, const int32_t* prefix, const GemmArgs& p,
                                             int lane, ItemPos& it, ItemLoads<MB, NBW>& ld) {
   constexpr int BM = 16 * MB;
@@ -180,8 +196,8 @@ __device__ __forceinline__ void decode_item(int32_t i, const int32_t* prefix, co
   for (int jb = 0; jb < NBW; ++jb) {
     const int32_t row = it.n0 + 16 * jb + c;
     const bool ok = row < n;
-    ld.w_voff[jb] = ok ? (uint32_t)(row * kb + 32 * g) : kOutOfRange;
-    ld.ws_voff[jb] = ok ? (uint32_t)(row * nbk + 4 * g) : kOutOfRange;
+    ld.w_voff[jb] = ok ? (uint32_t)(row * kb + 32 * KSUB * g) : kOutOfRange;
+    ld.ws_voff[jb] = ok ? (uint32_t)(row * nbk + 4 * KSUB * g) : kOutOfRange;
   }
   const sconst_i32 idx = (sconst_i32)p.a_row_index;
   const int32_t a_last = (int32_t)p.a_rows - 1;
@@ -201,34 +217,57 @@ __device__ __forceinline__ void decode_item(int32_t i, const int32_t* prefix, co
     int32_t mine = gather16<0>(0, src);
     mine = __builtin_amdgcn_ds_bpermute(c << 2, mine);
     mine = mine < 0 ? 0 : (mine > a_last ? a_last : mine);
-    ld.a_voff[ib] = (uint32_t)(mine * kb + 32 * g);
-    ld.as_voff[ib] = (uint32_t)(mine * nbk + 4 * g);
+    ld.a_voff[ib] = (uint32_t)(mine * kb + 32 * KSUB * g);
+    ld.as_voff[ib] = (uint32_t)(mine * nbk + 4 * KSUB * g);
   }
 }
 
-// Issue every load of one stage: K sub-steps kss .. kss+KSUB-1 (256 elements
-// each).  Unconditional, so the compiler can count outstanding loads exactly;
-// weight rows past n read zeros.  The per-lane offsets stay fixed for a whole
-// item and the K position goes in the scalar offset, so the loop writes no
-// VGPR that an in-flight load still reads.
+// The KSUB scale dwords of one lane, in one load.
+template <int KSUB>
+__device__ __forceinline__ void load_scales(uint32_t (&d)[KSUB], const rsrc_t& rs, uint32_t voff,
+                                            int32_t soff) {
+  if constexpr (KSUB == 1) {
+    d[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0);
+  } else if constexpr (KSUB == 2) {
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0);
+    d[0] = v[0];
+    d[1] = v[1];
+  } else {
+    static_assert(KSUB == 4, "stages of 256, 512 or 1024 K elements");
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0);
+    d[0] = v[0];
+    d[1] = v[1];
+    d[2] = v[2];
+    d[3] = v[3];
+  }
+}
+
+// Issue every load of stage `kst` of the current item.  Unconditional, so the
+// compiler can count outstanding loads exactly; weight rows past n read
+// zeros.  The per-lane offsets stay fixed for a whole item and the stage's K
+// position goes in the scalar offset, so the loop writes no VGPR that an
+// in-flight load still reads.
 template <int MB, int NBW, int KSUB>
 __device__ __forceinline__ void issue_loads(Stage<MB, NBW, KSUB>& st, const ItemLoads<MB, NBW>& it,
-                                            const rsrc_t& a_rs, const rsrc_t& as_rs, int32_t kss) {
+                                            const rsrc_t& a_rs, const rsrc_t& as_rs, int32_t kst) {
+  const int32_t qk = uniform(kst * 128 * KSUB), sk = uniform(kst * 16 * KSUB);
 #pragma unroll
-  for (int s = 0; s < KSUB; ++s) {
-    const int32_t qk = uniform((kss + s) * 128), sk = uniform((kss + s) * 16);
+  for (int jb = 0; jb < NBW; ++jb) {
 #pragma unroll
-    for (int jb = 0; jb < NBW; ++jb) {
-      st.w[jb][s][0] = __builtin_amdgcn_raw_buffer_load_b128(it.w, it.w_voff[jb], qk, 0);
-      st.w[jb][s][1] = __builtin_amdgcn_raw_buffer_load_b128(it.w, it.w_voff[jb] + 16u, qk, 0);
-      st.ws[jb][s] = __builtin_amdgcn_raw_buffer_load_b32(it.ws, it.ws_voff[jb], sk, 0);
+    for (int s = 0; s < KSUB; ++s) {
+      st.w[jb][s][0] = __builtin_amdgcn_raw_buffer_load_b128(it.w, it.w_voff[jb] + 32u * s, qk, 0);
+      st.w[jb][s][1] = __builtin_amdgcn_raw_buffer_load_b128(it.w, it.w_voff[jb] + 32u * s + 16u, qk, 0);
     }
+    load_scales<KSUB>(st.ws[jb], it.ws, it.ws_voff[jb], sk);
+  }
 #pragma unroll
-    for (int ib = 0; ib < MB; ++ib) {
-      st.a[ib][s][0] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, it.a_voff[ib], qk, 0);
-      st.a[ib][s][1] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, it.a_voff[ib] + 16u, qk, 0);
-      st.as[ib][s] = __builtin_amdgcn_raw_buffer_load_b32(as_rs, it.as_voff[ib], sk, 0);
+  for (int ib = 0; ib < MB; ++ib) {
+#pragma unroll
+    for (int s = 0; s < KSUB; ++s) {
+      st.a[ib][s][0] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, it.a_voff[ib] + 32u * s, qk, 0);
+      st.a[ib][s][1] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, it.a_voff[ib] + 32u * s + 16u, qk, 0);
     }
+    load_scales<KSUB>(st.as[ib], as_rs, it.as_voff[ib], sk);
   }
 }
 
@@ -379,7 +418,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_grouped_gemm(const GemmArgs p) {
   ItemPos ld_pos, cp;
   ItemLoads<MB, NBW> l0, l1;
   int32_t ld_round = 0, ld_st = 0, cp_st = 0;
-  decode_item<MB, NBW>(item_of(0), prefix, p, lane, ld_pos, l0);
+  decode_item<MB, NBW, KSUB>(item_of(0), prefix, p, lane, ld_pos, l0);
   cp = ld_pos;
   // Move the load position to the next unit: a new item is decoded into dst,
   // otherwise dst takes src's offsets.
@@ -387,7 +426,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_grouped_gemm(const GemmArgs p) {
     if (++ld_st == nst) {
       ld_st = 0;
       ++ld_round;
-      decode_item<MB, NBW>(item_of(ld_round), prefix, p, lane, ld_pos, dst);
+      decode_item<MB, NBW, KSUB>(item_of(ld_round), prefix, p, lane, ld_pos, dst);
     } else {
       dst = src;
     }
@@ -400,22 +439,23 @@ __global__ __launch_bounds__(WAVES * 64) void k_grouped_gemm(const GemmArgs p) {
     }
   };
 
-  // Two register stages.  Every iteration issues the next stage's loads (at
-  // the very end it re-reads the last stage, which the caches serve) before
-  // computing the current one, so one stage is always in flight.
+  // Two register stages.  Every iteration issues the next stage's loads before
+  // computing the current one, so one stage is always in flight; after the
+  // last unit the issue still happens (keeping the code free of branches
+  // around loads) but with out-of-range offsets, so it moves no data.
   Stage<MB, NBW, KSUB> s0, s1;
-  issue_loads<MB, NBW, KSUB>(s0, l0, a_rs, as_rs, ld_st * KSUB);
+  issue_loads<MB, NBW, KSUB>(s0, l0, a_rs, as_rs, ld_st);
   for (int32_t u = 0;; u += 2) {
     const bool more1 = u + 1 < units;
-    if (more1) advance(l1, l0); else l1 = l0;
-    issue_loads<MB, NBW, KSUB>(s1, l1, a_rs, as_rs, ld_st * KSUB);
+    if (more1) advance(l1, l0); else l1 = nowhere<MB, NBW>(l0);
+    issue_loads<MB, NBW, KSUB>(s1, l1, a_rs, as_rs, ld_st);
     compute_stage<MB, NBW, KSUB>(s0, cp, n, acc);
     hold<MB, NBW>(l0);
     retire();
     if (!more1) break;
     const bool more2 = u + 2 < units;
-    if (more2) advance(l0, l1); else l0 = l1;
-    issue_loads<MB, NBW, KSUB>(s0, l0, a_rs, as_rs, ld_st * KSUB);
+    if (more2) advance(l0, l1); else l0 = nowhere<MB, NBW>(l1);
+    issue_loads<MB, NBW, KSUB>(s0, l0, a_rs, as_rs, ld_st);
     compute_stage<MB, NBW, KSUB>(s1, cp, n, acc);
     hold<MB, NBW>(l1);
     retire();
@@ -508,7 +548,9 @@ GemmTile choose_tile(int32_t num_experts, int64_t m_total, int64_t n, int64_t k,
     }
     ok = ok && *s == '\0' && nv >= 2;
     ok = ok && (v[0] == 16 || v[0] == 32 || v[0] == 64) && (v[1] == 32 || v[1] == 64);
-    if (nv == 3) ok = ok && (v[2] == 256 || (v[2] == 512 && k % 512 == 0));
+    if (nv == 3)
+      ok = ok && (v[2] == 256 || (v[2] == 512 && k % 512 == 0) ||
+                  (v[2] == 1024 && k % 1024 == 0 && v[1] == 32 && v[0] <= 32));
     if (ok) {
       t.m_blocks = v[0] / 16;
       t.n_blocks = v[1] / 16;
@@ -532,13 +574,25 @@ hipError_t launch_mb(const GemmArgs& p, int m_blocks, hipStream_t stream) {
   }
 }
 
+// 1024-element stages: only for tiles whose two register stages still fit.
+template <>
+hipError_t launch_mb<2, 4>(const GemmArgs& p, int m_blocks, hipStream_t stream) {
+  switch (m_blocks) {
+    case 1: return launch_tile<1, 2, 4, 4>(p, stream);
+    case 2: return launch_tile<2, 2, 4, 4>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_grouped_gemm(const GemmArgs& p, const GemmTile& t, hipStream_t stream) {
   if (t.waves != 4 || p.k % (256 * t.k_sub) != 0) return hipErrorInvalidValue;
   if (t.n_blocks == 4) {
+    if (t.k_sub == 4) return hipErrorInvalidValue;
     return t.k_sub == 2 ? launch_mb<4, 2>(p, t.m_blocks, stream)
                         : launch_mb<4, 1>(p, t.m_blocks, stream);
   }
   if (t.n_blocks == 2) {
+    if (t.k_sub == 4) return launch_mb<2, 4>(p, t.m_blocks, stream);
     return t.k_sub == 2 ? launch_mb<2, 2>(p, t.m_blocks, stream)
                         : launch_mb<2, 1>(p, t.m_blocks, stream);
   }
