@@ -15,21 +15,22 @@
 //    weights are never read.  Items are numbered expert-major, N-tile, then
 //    M-tile fastest, so the M-tiles of one (expert, N-tile) run side by side
 //    and share that weight tile through L2.
-//  * Persistent wavefronts.  Every wavefront walks its own items (stride =
-//    number of wavefronts); no inter-wave synchronisation after the prefix.
-//    Workgroup ids are remapped so consecutive items land on the same XCD
-//    (the hardware deals workgroups round-robin over the 8 XCDs), keeping an
-//    expert's activation rows in one L2.
-//  * Loads.  K advances 256 elements per step.  For a 16-row block, lane
-//    (c = lane % 16, g = lane / 16) loads 32 contiguous bytes (64 codes) of row
-//    c at byte 32g of the step's 128-byte span, plus the 4 scale bytes of those
-//    64 codes: every 16-byte global load is a full-lane vector load straight
-//    into registers, already in MFMA operand order.  The contraction order
-//    over K is free, so MFMA t (0..7) of the step takes codes 8t..8t+7 of every
-//    lane; weights and activations use the same K order.
-//  * Pipelining.  The next (item, K-step) unit's loads are issued before the
-//    current unit is computed, across item boundaries too, so a wave keeps a
-//    step of loads in flight while it dequantises and multiplies.
+//  * Persistent wavefronts.  Every wavefront walks its own items in rounds of
+//    one item per wavefront, with no inter-wave synchronisation after the
+//    prefix; the workgroups active in a round are spread evenly over the XCDs.
+//  * Loads.  A pipeline stage covers 256*KSUB K elements.  Lane (c = lane %
+//    16, g = lane / 16) loads row c of each 16-row block, K run g of the stage,
+//    with 16-byte buffer loads that land in registers already in MFMA operand
+//    order.  Every load is unconditional (rows past n read zeros, a masked
+//    store is an out-of-range buffer offset), so the compiler's count of
+//    outstanding loads is exact and one stage stays in flight while the
+//    previous one is computed.
+//  * Weight block scales (SL).  For K a multiple of 2048, each wave copies the
+//    128-byte scale line of every weight row (one line = 2048 K elements) into
+//    its own LDS buffer with full-line buffer-to-LDS loads, double-buffered by
+//    span, and reads each stage's scales from there.  Loading the line in the
+//    per-stage pieces the MFMA needs would fetch every line in several pieces
+//    far apart in time, which costs several DRAM fetches per line.
 //  * Math.  Codes are dequantised exactly to FP16 (fp4_device.h) and fed to
 //    v_mfma_f32_16x16x32_f16 with FP32 accumulation: weights are the A operand
 //    (16 output columns), activations the B operand (16 rows).  The 16-element
@@ -58,11 +59,14 @@ constexpr int kXcds = 8;
 constexpr int kRawBufferWord3 = 0x00020000;
 // A buffer offset past every resource built here (each covers < 2^31 bytes).
 constexpr uint32_t kOutOfRange = 0x80000000u;
+// K elements whose block scales fill one 128-byte line of a row.
+constexpr int kSpan = 2048;
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 // Pointers the compiler reads through the scalar cache (uniform addresses).
 typedef const int32_t __attribute__((address_space(4)))* sconst_i32;
 typedef const float __attribute__((address_space(4)))* sconst_f32;
+typedef __attribute__((address_space(3))) void* lds_ptr;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
@@ -101,13 +105,22 @@ __device__ __forceinline__ int logical_block(int b, int nblk, int active) {
   return kXcds * pxa + xcd * (per_xcd - pxa) + (slot - pxa);
 }
 
+// LDS bytes per wave for staged weight scales: two span buffers of 16*NBW
+// rows x 128 bytes, and a 1 KB sink for the copies issued by stages that start
+// no span (see issue_loads).
+template <int NBW>
+constexpr int scale_lds_per_wave() {
+  return 2 * 16 * NBW * 128 + 1024;
+}
+
 // Register image of one pipeline stage (KSUB sub-steps of 256 K elements) for
 // one wavefront.  Within a stage, lane group g (lanes 16g .. 16g+15, one row
 // each) owns the contiguous K run [64*KSUB*g, 64*KSUB*(g+1)) of the stage: per
 // 16-row block and sub-step s, 32 code bytes (elements 64s .. 64s+63 of its
 // run) and one scale dword; the KSUB scale dwords of a lane are adjacent in
 // memory and arrive in one load.  Weights and activations use the same K
-// order, so every product pairs the same K element.
+// order, so every product pairs the same K element.  With SL the weight scales
+// come from LDS instead (ws is then filled by compute_stage).
 template <int MB, int NBW, int KSUB>
 struct Stage {
   u32x4_t w[NBW][KSUB][2];
@@ -132,6 +145,8 @@ struct ItemLoads {
   rsrc_t w, ws;
   uint32_t w_voff[NBW], ws_voff[NBW];  // lane's weight row, or out of range past n
   uint32_t a_voff[MB], as_voff[MB];    // lane's (gathered, clamped) activation row
+  uint32_t sl_voff;                    // lane's 16-byte piece of a scale-line copy
+  int32_t n0;
 };
 
 // An empty use of the lane offsets: keeps their registers allocated until the
@@ -144,6 +159,7 @@ __device__ __forceinline__ void hold(const ItemLoads<MB, NBW>& l) {
   for (int jb = 0; jb < NBW; ++jb) asm volatile("" ::"v"(l.w_voff[jb]), "v"(l.ws_voff[jb]));
 #pragma unroll
   for (int ib = 0; ib < MB; ++ib) asm volatile("" ::"v"(l.a_voff[ib]), "v"(l.as_voff[ib]));
+  asm volatile("" ::"v"(l.sl_voff));
 }
 
 // The same loads with every offset out of range: they return zeros without a
@@ -155,6 +171,8 @@ __device__ __forceinline__ ItemLoads<MB, NBW> nowhere(const ItemLoads<MB, NBW>& 
   for (int jb = 0; jb < NBW; ++jb) z.w_voff[jb] = z.ws_voff[jb] = kOutOfRange;
 #pragma unroll
   for (int ib = 0; ib < MB; ++ib) z.a_voff[ib] = z.as_voff[ib] = kOutOfRange;
+  z.sl_voff = kOutOfRange;
+  z.n0 = 0x40000000;  // no scale-line copy either
   return z;
 }
 
@@ -192,12 +210,20 @@ __device__ __forceinline__ void decode_item(int32_t i, const int32_t* prefix, co
   const int32_t n = (int32_t)p.n, kb = (int32_t)(p.k >> 1), nbk = (int32_t)(p.k >> 4);
   ld.w = make_rsrc(p.w_q + (int64_t)lo * n * kb, (uint32_t)(n * kb));
   ld.ws = make_rsrc(p.w_sf + (int64_t)lo * n * nbk, (uint32_t)(n * nbk));
+  ld.n0 = it.n0;
 #pragma unroll
   for (int jb = 0; jb < NBW; ++jb) {
     const int32_t row = it.n0 + 16 * jb + c;
     const bool ok = row < n;
     ld.w_voff[jb] = ok ? (uint32_t)(row * kb + 32 * KSUB * g) : kOutOfRange;
     ld.ws_voff[jb] = ok ? (uint32_t)(row * nbk + 4 * KSUB * g) : kOutOfRange;
+  }
+  // Scale-line copies move 8 rows x 128 bytes per instruction: lane l takes
+  // row l/8 and stores the row's 16-byte chunk (l%8) ^ (row%8) in LDS slot l%8,
+  // a swizzle that spreads the later per-stage reads over the LDS banks.
+  {
+    const int r8 = lane >> 3, slot = lane & 7;
+    ld.sl_voff = (uint32_t)((it.n0 + r8) * nbk + 16 * (slot ^ r8));
   }
   const sconst_i32 idx = (sconst_i32)p.a_row_index;
   const int32_t a_last = (int32_t)p.a_rows - 1;
@@ -242,14 +268,36 @@ __device__ __forceinline__ void load_scales(uint32_t (&d)[KSUB], const rsrc_t& r
   }
 }
 
+// Where the scale-line copy of a stage goes: the buffer of its span when the
+// stage starts a span (sl_span >= 0), else the sink, with no data moved.
+struct LineCopy {
+  uint8_t* dst;     // LDS: span buffer or sink (wavefront-uniform)
+  int32_t span;     // span of the item the copy reads, or -1 for none
+};
+
 // Issue every load of stage `kst` of the current item.  Unconditional, so the
 // compiler can count outstanding loads exactly; weight rows past n read
 // zeros.  The per-lane offsets stay fixed for a whole item and the stage's K
 // position goes in the scalar offset, so the loop writes no VGPR that an
-// in-flight load still reads.
-template <int MB, int NBW, int KSUB>
+// in-flight load still reads.  With SL, the stage first copies the 128-byte
+// scale lines of the item's 16*NBW weight rows for its span into LDS, or, if
+// it starts no span, issues the same copies out of range into the sink.
+template <int MB, int NBW, int KSUB, bool SL>
 __device__ __forceinline__ void issue_loads(Stage<MB, NBW, KSUB>& st, const ItemLoads<MB, NBW>& it,
-                                            const rsrc_t& a_rs, const rsrc_t& as_rs, int32_t kst) {
+                                            const rsrc_t& a_rs, const rsrc_t& as_rs, int32_t kst,
+                                            const LineCopy& lc, int32_t n, int32_t nbk) {
+  if constexpr (SL) {
+    const bool on = lc.span >= 0;
+    const int32_t soff = uniform(on ? lc.span * 128 : 0);
+#pragma unroll
+    for (int i = 0; i < 2 * NBW; ++i) {
+      // Rows 8i .. 8i+7 of the tile: all inside n or all outside (n % 16 == 0).
+      const bool rows_ok = on && it.n0 + 8 * i < n;
+      const uint32_t voff = rows_ok ? it.sl_voff + (uint32_t)(8 * i * nbk) : kOutOfRange;
+      uint8_t* dst = on ? lc.dst + 1024 * i : lc.dst;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(it.ws, (lds_ptr)dst, 16, voff, soff, 0, 0);
+    }
+  }
   const int32_t qk = uniform(kst * 128 * KSUB), sk = uniform(kst * 16 * KSUB);
 #pragma unroll
   for (int jb = 0; jb < NBW; ++jb) {
@@ -258,7 +306,7 @@ __device__ __forceinline__ void issue_loads(Stage<MB, NBW, KSUB>& st, const Item
       st.w[jb][s][0] = __builtin_amdgcn_raw_buffer_load_b128(it.w, it.w_voff[jb] + 32u * s, qk, 0);
       st.w[jb][s][1] = __builtin_amdgcn_raw_buffer_load_b128(it.w, it.w_voff[jb] + 32u * s + 16u, qk, 0);
     }
-    load_scales<KSUB>(st.ws[jb], it.ws, it.ws_voff[jb], sk);
+    if constexpr (!SL) load_scales<KSUB>(st.ws[jb], it.ws, it.ws_voff[jb], sk);
   }
 #pragma unroll
   for (int ib = 0; ib < MB; ++ib) {
@@ -271,8 +319,93 @@ __device__ __forceinline__ void issue_loads(Stage<MB, NBW, KSUB>& st, const Item
   }
 }
 
+// LDS byte address of a shared-memory pointer.
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const uint8_t*)p);
+}
+
+// NBW LDS reads of one width at `addr` + 2048 * jb (row blocks are 16 rows x
+// 128 bytes apart), then a wait for all of them, in one asm statement: the
+// compiler sees neither an LDS read it would order after the in-flight
+// buffer-to-LDS copies nor outputs it could use before the wait.  `dep` is a
+// register of the stage's last load, so the compiler waits for that load
+// first (and with it, in issue order, for the stage's own line copy).
+#define MOE_FP4_LDS_READ2(OP, T)                                                      \
+  {                                                                                 \
+    T r0, r1;                                                                       \
+    asm volatile(OP " %0, %2\n\t" OP " %1, %2 offset:2048\n\ts_waitcnt lgkmcnt(0)"  \
+                 : "=&v"(r0), "=&v"(r1)                                             \
+                 : "v"(addr), "v"(dep));                                            \
+    out[0] = r0;                                                                    \
+    out[1] = r1;                                                                    \
+  }
+#define MOE_FP4_LDS_READ4(OP, T)                                                    \
+  {                                                                                 \
+    T r0, r1, r2, r3;                                                               \
+    asm volatile(OP " %0, %4\n\t" OP " %1, %4 offset:2048\n\t" OP                   \
+                    " %2, %4 offset:4096\n\t" OP                                    \
+                    " %3, %4 offset:6144\n\ts_waitcnt lgkmcnt(0)"                   \
+                 : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)                       \
+                 : "v"(addr), "v"(dep));                                            \
+    out[0] = r0;                                                                    \
+    out[1] = r1;                                                                    \
+    out[2] = r2;                                                                    \
+    out[3] = r3;                                                                    \
+  }
+
+template <int NBW, typename T>
+__device__ __forceinline__ void lds_read_rows(T (&out)[NBW], uint32_t addr, uint32_t dep) {
+  if constexpr (sizeof(T) == 4) {
+    if constexpr (NBW == 2) MOE_FP4_LDS_READ2("ds_read_b32", T) else MOE_FP4_LDS_READ4("ds_read_b32", T)
+  } else if constexpr (sizeof(T) == 8) {
+    if constexpr (NBW == 2) MOE_FP4_LDS_READ2("ds_read_b64", T) else MOE_FP4_LDS_READ4("ds_read_b64", T)
+  } else {
+    if constexpr (NBW == 2) MOE_FP4_LDS_READ2("ds_read_b128", T) else MOE_FP4_LDS_READ4("ds_read_b128", T)
+  }
+}
+#undef MOE_FP4_LDS_READ2
+#undef MOE_FP4_LDS_READ4
+
+// Weight scales of one stage from the LDS span buffer `buf` (stage j of its
+// span): lane (c, g) of block jb reads row 16*jb + c, bytes 16*KSUB*j +
+// 4*KSUB*g .. +4*KSUB of the line, which the copy stored with its 16-byte
+// chunks swizzled by row.
+template <int NBW, int KSUB>
+__device__ __forceinline__ void read_line_scales(uint32_t (&ws)[NBW][KSUB], const uint8_t* buf,
+                                                 int32_t j, int c, int g, uint32_t dep) {
+  const int o = 16 * KSUB * j + 4 * KSUB * g;
+  const int chunk = (o >> 4) ^ (c & 7), within = o & 15;
+  const uint32_t addr = lds_addr(buf) + (uint32_t)(c * 128 + 16 * chunk + within);
+  if constexpr (KSUB == 1) {
+    uint32_t r[NBW];
+    lds_read_rows<NBW>(r, addr, dep);
+#pragma unroll
+    for (int jb = 0; jb < NBW; ++jb) ws[jb][0] = r[jb];
+  } else if constexpr (KSUB == 2) {
+    u32x2_t r[NBW];
+    lds_read_rows<NBW>(r, addr, dep);
+#pragma unroll
+    for (int jb = 0; jb < NBW; ++jb) {
+      ws[jb][0] = r[jb][0];
+      ws[jb][1] = r[jb][1];
+    }
+  } else {
+    u32x4_t r[NBW];
+    lds_read_rows<NBW>(r, addr, dep);
+#pragma unroll
+    for (int jb = 0; jb < NBW; ++jb) {
+      ws[jb][0] = r[jb][0];
+      ws[jb][1] = r[jb][1];
+      ws[jb][2] = r[jb][2];
+      ws[jb][3] = r[jb][3];
+    }
+  }
+}
+
 template <int MB, int NBW, int KSUB>
 __device__ __forceinline__ void compute_stage(const Stage<MB, NBW, KSUB>& st,
+                                              const uint32_t (&wsd)[NBW][KSUB],
                                               const ItemPos& it, int32_t n,
                                               float4_t (&acc)[NBW][MB]) {
 #pragma unroll
@@ -281,8 +414,8 @@ __device__ __forceinline__ void compute_stage(const Stage<MB, NBW, KSUB>& st,
     half2_t wsc[NBW][2], asc[MB][2];
 #pragma unroll
     for (int jb = 0; jb < NBW; ++jb) {
-      wsc[jb][0] = scale_pair_x2m8<false>(st.ws[jb][s]);
-      wsc[jb][1] = scale_pair_x2m8<true>(st.ws[jb][s]);
+      wsc[jb][0] = scale_pair_x2m8<false>(wsd[jb][s]);
+      wsc[jb][1] = scale_pair_x2m8<true>(wsd[jb][s]);
     }
 #pragma unroll
     for (int ib = 0; ib < MB; ++ib) {
@@ -338,11 +471,17 @@ __device__ __forceinline__ void epilogue(float4_t (&acc)[NBW][MB], const ItemPos
   }
 }
 
-template <int MB, int NBW, int KSUB, int WAVES>
+// LDS layout: the work-list prefix, then (with SL) each wave's scale buffers.
+__host__ __device__ constexpr size_t prefix_bytes(int num_experts) {
+  return ((size_t)(num_experts + 1) * 4 + 15) / 16 * 16;
+}
+
+template <int MB, int NBW, int KSUB, int WAVES, bool SL>
 __global__ __launch_bounds__(WAVES * 64) void k_grouped_gemm(const GemmArgs p) {
   constexpr int BM = 16 * MB;
   constexpr int NTHR = WAVES * 64;
-  extern __shared__ int32_t prefix[];  // [num_experts + 1] item prefix
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  int32_t* prefix = reinterpret_cast<int32_t*>(smem);  // [num_experts + 1] item prefix
   __shared__ int32_t wave_sum[WAVES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);  // the compiler cannot see that this is wave-uniform
@@ -402,10 +541,25 @@ __global__ __launch_bounds__(WAVES * 64) void k_grouped_gemm(const GemmArgs p) {
   const int c = lane & 15, g = lane >> 4;
   const int32_t nsub = (int32_t)(p.k / 256);    // 256-element sub-steps per row
   const int32_t nst = nsub / KSUB;              // stages per item
-  const int32_t units = my_items * nst;  // < 2^31 (host bound on items * stages)
+  const int32_t units = my_items * nst;         // < 2^31 (host bound on items * stages)
   const rsrc_t a_rs = make_rsrc(p.a_q, (uint32_t)(p.a_rows * (p.k >> 1)));
   const rsrc_t as_rs = make_rsrc(p.a_sf, (uint32_t)(p.a_rows * (p.k >> 4)));
-  const int32_t n = (int32_t)p.n;
+  const int32_t n = (int32_t)p.n, nbk = (int32_t)(p.k >> 4);
+
+  // This wave's scale-line buffers (SL): span buffers 0 and 1, then the sink.
+  constexpr int kSpanStages = kSpan / (256 * KSUB);  // stages per span
+  constexpr int kBufBytes = 16 * NBW * 128;
+  uint8_t* const sl_base = smem + prefix_bytes(E) + (size_t)wave * scale_lds_per_wave<NBW>();
+  auto line_copy = [&](int32_t round, int32_t st) -> LineCopy {
+    LineCopy lc;
+    const bool start = st % kSpanStages == 0;
+    const int32_t span = st / kSpanStages;
+    const int32_t nsp = nst / kSpanStages;
+    const int32_t buf = (round * nsp + span) & 1;
+    lc.dst = start ? sl_base + buf * kBufBytes : sl_base + 2 * kBufBytes;
+    lc.span = start ? span : -1;
+    return lc;
+  };
 
   float4_t acc[NBW][MB];
 #pragma unroll
@@ -417,7 +571,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_grouped_gemm(const GemmArgs p) {
   // Each register stage has its own set of lane offsets (l0 for s0, l1 for s1).
   ItemPos ld_pos, cp;
   ItemLoads<MB, NBW> l0, l1;
-  int32_t ld_round = 0, ld_st = 0, cp_st = 0;
+  int32_t ld_round = 0, ld_st = 0, cp_round = 0, cp_st = 0;
   decode_item<MB, NBW, KSUB>(item_of(0), prefix, p, lane, ld_pos, l0);
   cp = ld_pos;
   // Move the load position to the next unit: a new item is decoded into dst,
@@ -435,7 +589,24 @@ __global__ __launch_bounds__(WAVES * 64) void k_grouped_gemm(const GemmArgs p) {
     if (++cp_st == nst) {
       epilogue<MB, NBW>(acc, cp, c, g, p);
       cp_st = 0;
+      ++cp_round;
       cp = ld_pos;
+    }
+  };
+  // Weight scales of the stage about to be computed.
+  auto stage_scales = [&](const Stage<MB, NBW, KSUB>& st, uint32_t (&wsd)[NBW][KSUB]) {
+    if constexpr (SL) {
+      const int32_t nsp = nst / kSpanStages;
+      const int32_t buf = (cp_round * nsp + cp_st / kSpanStages) & 1;
+      // The stage's last load (the activation scales) orders the read after
+      // the stage's line copy: loads complete in issue order.
+      read_line_scales<NBW, KSUB>(wsd, sl_base + buf * kBufBytes, cp_st % kSpanStages, c, g,
+                                  st.as[MB - 1][KSUB - 1]);
+    } else {
+#pragma unroll
+      for (int jb = 0; jb < NBW; ++jb)
+#pragma unroll
+        for (int s = 0; s < KSUB; ++s) wsd[jb][s] = st.ws[jb][s];
     }
   };
 
@@ -444,19 +615,26 @@ __global__ __launch_bounds__(WAVES * 64) void k_grouped_gemm(const GemmArgs p) {
   // last unit the issue still happens (keeping the code free of branches
   // around loads) but with out-of-range offsets, so it moves no data.
   Stage<MB, NBW, KSUB> s0, s1;
-  issue_loads<MB, NBW, KSUB>(s0, l0, a_rs, as_rs, ld_st);
+  uint32_t wsd[NBW][KSUB];
+  issue_loads<MB, NBW, KSUB, SL>(s0, l0, a_rs, as_rs, ld_st, line_copy(ld_round, ld_st), n, nbk);
   for (int32_t u = 0;; u += 2) {
     const bool more1 = u + 1 < units;
     if (more1) advance(l1, l0); else l1 = nowhere<MB, NBW>(l0);
-    issue_loads<MB, NBW, KSUB>(s1, l1, a_rs, as_rs, ld_st);
-    compute_stage<MB, NBW, KSUB>(s0, cp, n, acc);
+    issue_loads<MB, NBW, KSUB, SL>(s1, l1, a_rs, as_rs, ld_st,
+                                   more1 ? line_copy(ld_round, ld_st) : LineCopy{sl_base + 2 * kBufBytes, -1},
+                                   n, nbk);
+    stage_scales(s0, wsd);
+    compute_stage<MB, NBW, KSUB>(s0, wsd, cp, n, acc);
     hold<MB, NBW>(l0);
     retire();
     if (!more1) break;
     const bool more2 = u + 2 < units;
     if (more2) advance(l0, l1); else l0 = nowhere<MB, NBW>(l1);
-    issue_loads<MB, NBW, KSUB>(s0, l0, a_rs, as_rs, ld_st);
-    compute_stage<MB, NBW, KSUB>(s1, cp, n, acc);
+    issue_loads<MB, NBW, KSUB, SL>(s0, l0, a_rs, as_rs, ld_st,
+                                   more2 ? line_copy(ld_round, ld_st) : LineCopy{sl_base + 2 * kBufBytes, -1},
+                                   n, nbk);
+    stage_scales(s1, wsd);
+    compute_stage<MB, NBW, KSUB>(s1, wsd, cp, n, acc);
     hold<MB, NBW>(l1);
     retire();
     if (!more2) break;
@@ -504,10 +682,10 @@ hipError_t resident_groups(K kern, int threads, size_t lds, int* out) {
   return hipSuccess;
 }
 
-template <int MB, int NBW, int KSUB, int WAVES>
+template <int MB, int NBW, int KSUB, int WAVES, bool SL>
 hipError_t launch_tile(const GemmArgs& p, hipStream_t stream) {
-  auto kern = k_grouped_gemm<MB, NBW, KSUB, WAVES>;
-  const size_t lds = sizeof(int32_t) * ((size_t)p.num_experts + 1);
+  auto kern = k_grouped_gemm<MB, NBW, KSUB, WAVES, SL>;
+  const size_t lds = prefix_bytes(p.num_experts) + (SL ? (size_t)WAVES * scale_lds_per_wave<NBW>() : 0);
   int resident = 0;
   hipError_t err = resident_groups(kern, WAVES * 64, lds, &resident);
   if (err != hipSuccess) return err;
@@ -528,13 +706,16 @@ hipError_t launch_tile(const GemmArgs& p, hipStream_t stream) {
 
 GemmTile choose_tile(int32_t num_experts, int64_t m_total, int64_t n, int64_t k, const char* env) {
   (void)n;
-  GemmTile t{1, 4, 4, 1};
+  GemmTile t{1, 4, 4, 1, 0};
   const int64_t avg = num_experts > 0 ? (m_total + num_experts - 1) / num_experts : m_total;
   if (avg > 32) t.m_blocks = 4;
   else if (avg > 16) t.m_blocks = 2;
   if (k % 512 == 0) t.k_sub = 2;
+  t.lds_scales = k % kSpan == 0 ? 1 : 0;
   if (env && *env) {
-    // "MxN" or "MxNxK": M rows per item, N columns per wave, K elements per stage.
+    // "MxN" or "MxNxK", optionally followed by 'r' (weight scales through
+    // registers rather than LDS): M rows per item, N columns per wave, K
+    // elements per stage.
     int v[3] = {0, 0, 0};
     int nv = 0;
     const char* s = env;
@@ -543,9 +724,11 @@ GemmTile choose_tile(int32_t num_experts, int64_t m_total, int64_t n, int64_t k,
       if (*s < '0' || *s > '9') { ok = false; break; }
       while (*s >= '0' && *s <= '9') v[nv] = v[nv] * 10 + (*s++ - '0');
       ++nv;
-      if (*s == '\0') break;
+      if (*s == '\0' || *s == 'r') break;
       if (*s == 'x' || *s == 'X') ++s; else ok = false;
     }
+    const bool regs = ok && *s == 'r';
+    if (regs) ++s;
     ok = ok && *s == '\0' && nv >= 2;
     ok = ok && (v[0] == 16 || v[0] == 32 || v[0] == 64) && (v[1] == 32 || v[1] == 64);
     if (nv == 3)
@@ -555,48 +738,60 @@ GemmTile choose_tile(int32_t num_experts, int64_t m_total, int64_t n, int64_t k,
       t.m_blocks = v[0] / 16;
       t.n_blocks = v[1] / 16;
       if (nv == 3) t.k_sub = v[2] / 256;
+      if (regs) t.lds_scales = 0;
     }
   }
   return t;
 }
 
 int64_t gemm_lds_bytes(const GemmTile& t, int32_t num_experts) {
-  return (int64_t)sizeof(int32_t) * ((int64_t)num_experts + 1 + t.waves);
+  int64_t b = (int64_t)prefix_bytes(num_experts) + (int64_t)sizeof(int32_t) * t.waves;
+  if (t.lds_scales) b += (int64_t)t.waves * (2 * 16 * 16 * t.n_blocks * 8 + 1024);
+  return b;
 }
 
-template <int NBW, int KSUB>
+template <int NBW, int KSUB, bool SL>
 hipError_t launch_mb(const GemmArgs& p, int m_blocks, hipStream_t stream) {
   switch (m_blocks) {
-    case 1: return launch_tile<1, NBW, KSUB, 4>(p, stream);
-    case 2: return launch_tile<2, NBW, KSUB, 4>(p, stream);
-    case 4: return launch_tile<4, NBW, KSUB, 4>(p, stream);
+    case 1: return launch_tile<1, NBW, KSUB, 4, SL>(p, stream);
+    case 2: return launch_tile<2, NBW, KSUB, 4, SL>(p, stream);
+    case 4: return launch_tile<4, NBW, KSUB, 4, SL>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 // 1024-element stages: only for tiles whose two register stages still fit.
-template <>
-hipError_t launch_mb<2, 4>(const GemmArgs& p, int m_blocks, hipStream_t stream) {
+template <bool SL>
+hipError_t launch_mb_k1024(const GemmArgs& p, int m_blocks, hipStream_t stream) {
   switch (m_blocks) {
-    case 1: return launch_tile<1, 2, 4, 4>(p, stream);
-    case 2: return launch_tile<2, 2, 4, 4>(p, stream);
+    case 1: return launch_tile<1, 2, 4, 4, SL>(p, stream);
+    case 2: return launch_tile<2, 2, 4, 4, SL>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_grouped_gemm(const GemmArgs& p, const GemmTile& t, hipStream_t stream) {
-  if (t.waves != 4 || p.k % (256 * t.k_sub) != 0) return hipErrorInvalidValue;
+template <bool SL>
+hipError_t launch_sl(const GemmArgs& p, const GemmTile& t, hipStream_t stream) {
   if (t.n_blocks == 4) {
     if (t.k_sub == 4) return hipErrorInvalidValue;
-    return t.k_sub == 2 ? launch_mb<4, 2>(p, t.m_blocks, stream)
-                        : launch_mb<4, 1>(p, t.m_blocks, stream);
+    return t.k_sub == 2 ? launch_mb<4, 2, SL>(p, t.m_blocks, stream)
+                        : launch_mb<4, 1, SL>(p, t.m_blocks, stream);
   }
   if (t.n_blocks == 2) {
-    if (t.k_sub == 4) return launch_mb<2, 4>(p, t.m_blocks, stream);
-    return t.k_sub == 2 ? launch_mb<2, 2>(p, t.m_blocks, stream)
-                        : launch_mb<2, 1>(p, t.m_blocks, stream);
+    if (t.k_sub == 4) return launch_mb_k1024<SL>(p, t.m_blocks, stream);
+    return t.k_sub == 2 ? launch_mb<2, 2, SL>(p, t.m_blocks, stream)
+                        : launch_mb<2, 1, SL>(p, t.m_blocks, stream);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_grouped_gemm(const GemmArgs& p, const GemmTile& t, hipStream_t stream) {
+  if (t.waves != 4 || p.k % (256 * t.k_sub) != 0) return hipErrorInvalidValue;
+  if (t.lds_scales) {
+    if (p.k % kSpan != 0) return hipErrorInvalidValue;
+    return launch_sl<true>(p, t, stream);
+  }
+  return launch_sl<false>(p, t, stream);
 }
 
 }  // namespace moe_fp4

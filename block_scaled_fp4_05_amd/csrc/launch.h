@@ -21,13 +21,15 @@ struct GemmTile {
   int n_blocks;
   int waves;
   int k_sub;
+  int lds_scales;  // weight block scales staged through LDS (needs k % 2048 == 0)
 };
 
 constexpr int kKStep = 256;  // K granularity the kernels require
 
 // The tile used for a problem with these sizes; `env` (may be NULL) is the
 // value of MOE_FP4_TILE ("MxN" or "MxNxK": M rows per item, N columns per
-// wave, K elements per pipeline stage).
+// wave, K elements per pipeline stage; a trailing 'r' keeps the weight block
+// scales in registers instead of staging them through LDS).
 GemmTile choose_tile(int32_t num_experts, int64_t m_total, int64_t n, int64_t k, const char* env);
 
 // LDS bytes a workgroup of the grouped GEMM uses for `num_experts` experts.
