@@ -403,10 +403,9 @@ __device__ __forceinline__ void read_line_scales(uint32_t (&ws)[NBW][KSUB], cons
   }
 }
 
-template <int MB, int NBW, int KSUB>
+template <int MB, int NBW, int KSUB, bool SKIP>
 __device__ __forceinline__ void compute_stage(const Stage<MB, NBW, KSUB>& st,
-                                              const uint32_t (&wsd)[NBW][KSUB],
-                                              const ItemPos& it, int32_t n,
+                                              const uint32_t (&wsd)[NBW][KSUB], int32_t rows_valid,
                                               float4_t (&acc)[NBW][MB]) {
 #pragma unroll
   for (int s = 0; s < KSUB; ++s) {
@@ -429,31 +428,59 @@ __device__ __forceinline__ void compute_stage(const Stage<MB, NBW, KSUB>& st,
 #pragma unroll
       for (int ib = 0; ib < MB; ++ib)
         af[ib] = dequant8(st.a[ib][s][half][word], asc[ib][spair][sidx]);
+      // Column blocks past n hold zeros and rows past the expert repeat its
+      // first row; neither is stored.  With SKIP, row blocks wholly past the
+      // expert skip their MFMAs (a uniform branch).  Without it every loaded
+      // register is consumed on every path: a load whose result some path
+      // skipped would look pending to the compiler on the next iteration and
+      // cost a wait there, which matters when items end every stage or two.
 #pragma unroll
       for (int jb = 0; jb < NBW; ++jb) {
-        if (it.n0 + 16 * jb < n) {  // uniform: skip column blocks past n
-          const half8_t wf = dequant8(st.w[jb][s][half][word], wsc[jb][spair][sidx]);
+        const half8_t wf = dequant8(st.w[jb][s][half][word], wsc[jb][spair][sidx]);
 #pragma unroll
-          for (int ib = 0; ib < MB; ++ib) {
-            if (16 * ib < it.rows_valid)  // uniform: skip row blocks past the expert
-              acc[jb][ib] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf, af[ib], acc[jb][ib], 0, 0, 0);
-          }
+        for (int ib = 0; ib < MB; ++ib) {
+          if (!SKIP || 16 * ib < rows_valid)
+            acc[jb][ib] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf, af[ib], acc[jb][ib], 0, 0, 0);
         }
       }
     }
   }
 }
 
+// Registers the stores of the last finished item read: kept allocated (see
+// hold_stores) until a later wait shows the stores complete, so no following
+// instruction overwrites them while a store may still be reading them.
+template <int MB, int NBW>
+struct PendingStores {
+  u32x2_t data[NBW][MB];
+  uint32_t voff[MB];
+};
+
+template <int MB, int NBW>
+__device__ __forceinline__ void hold_stores(const PendingStores<MB, NBW>& ps) {
+#pragma unroll
+  for (int ib = 0; ib < MB; ++ib) {
+    asm volatile("" ::"v"(ps.voff[ib]));
+#pragma unroll
+    for (int jb = 0; jb < NBW; ++jb) asm volatile("" ::"v"(ps.data[jb][ib]));
+  }
+}
+
 // BF16 store of a finished item.  Lane (c, g) holds rows 16*ib + c, columns
 // 16*jb + 4g .. +3.  Stores go through a buffer resource covering exactly the
 // item's valid rows, so rows past the expert's end fall outside it and are
-// dropped; column blocks past n get an out-of-range offset.  No branches.
+// dropped; a column block past n (uniform) is skipped.
 template <int MB, int NBW>
 __device__ __forceinline__ void epilogue(float4_t (&acc)[NBW][MB], const ItemPos& it,
-                                         int c, int g, const GemmArgs& p) {
+                                         int c, int g, const GemmArgs& p,
+                                         PendingStores<MB, NBW>& ps) {
   typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-  const rsrc_t o = make_rsrc(p.out + (int64_t)it.row0 * p.ldo,
-                             (uint32_t)((int64_t)it.rows_valid * p.ldo * 2));
+  const int32_t ldo = (int32_t)p.ldo;
+  const rsrc_t o = make_rsrc(p.out + (int64_t)it.row0 * ldo,
+                             (uint32_t)((int64_t)it.rows_valid * ldo * 2));
+#pragma unroll
+  for (int ib = 0; ib < MB; ++ib)
+    ps.voff[ib] = (uint32_t)(((16 * ib + c) * ldo + it.n0 + 4 * g) * 2);
 #pragma unroll
   for (int jb = 0; jb < NBW; ++jb) {
 #pragma unroll
@@ -461,12 +488,13 @@ __device__ __forceinline__ void epilogue(float4_t (&acc)[NBW][MB], const ItemPos
       const float4_t v = acc[jb][ib];
       const bf16x4_t b = {(__bf16)(v[0] * it.alpha), (__bf16)(v[1] * it.alpha),
                           (__bf16)(v[2] * it.alpha), (__bf16)(v[3] * it.alpha)};
-      const int32_t col = it.n0 + 16 * jb;
-      const uint32_t off = col < (int32_t)p.n
-          ? (uint32_t)(((16 * ib + c) * (int32_t)p.ldo + col + 4 * g) * 2)
-          : kOutOfRange;
-      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, b), o, off, 0, 0);
+      ps.data[jb][ib] = __builtin_bit_cast(u32x2_t, b);
       acc[jb][ib] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    if (it.n0 + 16 * jb < (int32_t)p.n) {
+#pragma unroll
+      for (int ib = 0; ib < MB; ++ib)
+        __builtin_amdgcn_raw_buffer_store_b64(ps.data[jb][ib], o, ps.voff[ib] + 32u * jb, 0, 0);
     }
   }
 }
@@ -585,9 +613,16 @@ __global__ __launch_bounds__(WAVES * 64) void k_grouped_gemm(const GemmArgs p) {
       dst = src;
     }
   };
+  PendingStores<MB, NBW> ps;
+#pragma unroll
+  for (int ib = 0; ib < MB; ++ib) {
+    ps.voff[ib] = 0;
+#pragma unroll
+    for (int jb = 0; jb < NBW; ++jb) ps.data[jb][ib] = u32x2_t{0u, 0u};
+  }
   auto retire = [&]() {
     if (++cp_st == nst) {
-      epilogue<MB, NBW>(acc, cp, c, g, p);
+      epilogue<MB, NBW>(acc, cp, c, g, p, ps);
       cp_st = 0;
       ++cp_round;
       cp = ld_pos;
@@ -623,9 +658,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_grouped_gemm(const GemmArgs p) {
     issue_loads<MB, NBW, KSUB, SL>(s1, l1, a_rs, as_rs, ld_st,
                                    more1 ? line_copy(ld_round, ld_st) : LineCopy{sl_base + 2 * kBufBytes, -1},
                                    n, nbk);
+    // Without the uniform branches of SL kernels, keep the scheduler from
+    // sinking the next stage's loads into (or below) this stage's computation.
+    if constexpr (!SL) __builtin_amdgcn_sched_barrier(0);
     stage_scales(s0, wsd);
-    compute_stage<MB, NBW, KSUB>(s0, wsd, cp, n, acc);
+    compute_stage<MB, NBW, KSUB, SL>(s0, wsd, cp.rows_valid, acc);
     hold<MB, NBW>(l0);
+    if constexpr (!SL) hold_stores<MB, NBW>(ps);
     retire();
     if (!more1) break;
     const bool more2 = u + 2 < units;
@@ -633,9 +672,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_grouped_gemm(const GemmArgs p) {
     issue_loads<MB, NBW, KSUB, SL>(s0, l0, a_rs, as_rs, ld_st,
                                    more2 ? line_copy(ld_round, ld_st) : LineCopy{sl_base + 2 * kBufBytes, -1},
                                    n, nbk);
+    if constexpr (!SL) __builtin_amdgcn_sched_barrier(0);
     stage_scales(s1, wsd);
-    compute_stage<MB, NBW, KSUB>(s1, wsd, cp, n, acc);
+    compute_stage<MB, NBW, KSUB, SL>(s1, wsd, cp.rows_valid, acc);
     hold<MB, NBW>(l1);
+    if constexpr (!SL) hold_stores<MB, NBW>(ps);
     retire();
     if (!more2) break;
   }
