@@ -14,6 +14,9 @@ case, where every layer's experts differ from the previous one's).
 
 Prints ONE JSON line (the value is whole-step TFLOP/s; the GEMM kernel's HBM
 roofline and the CPU oracle's throughput on the same workload ride along).
+Kernel durations come from HIP events around back-to-back launches of that
+kernel alone on the launch stream (rocprofv3's per-kernel average measures
+the same thing).
 
   python bench.py [--steps K] [--warmup W] [--workload c3] [--secondary c4]
   python bench.py --copy-calibration   # a plain copy of known size, for counter scaling
@@ -147,26 +150,51 @@ class Problem:
 
 
 def measure(prob, steps, warmup):
-    """Time `steps` whole steps after `warmup` untimed ones.  Returns the wall time
-    per step and the per-kernel averages from HIP events on the launch stream."""
+    """Time `steps` whole steps after `warmup` untimed ones, then the two kernels
+    of the path on their own (each launched `steps` times back to back between
+    two HIP events on the launch stream, so per-launch event overhead does not
+    inflate a kernel's duration).  Returns wall time per step and per-kernel
+    averages."""
     import torch
+    from block_scaled_fp4_05_amd import moe_fp4
     for i in range(warmup):
         prob.step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record()
     for i in range(steps):
-        prob.step(warmup + i, evs[i])
+        prob.step(warmup + i)
+    e1.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    quant_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    gemm_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    region_ms = evs[0][0].elapsed_time(evs[-1][2])
-    return dict(wall_ms_per_step=(t1 - t0) * 1e3 / steps,
-                gpu_ms_per_step=region_ms / steps,
-                quant_ms=sum(quant_ms) / steps, gemm_ms=sum(gemm_ms) / steps,
-                gemm_ms_min=min(gemm_ms), gemm_ms_max=max(gemm_ms))
+    region_ms = e0.elapsed_time(e1)
+
+    def back_to_back(fn):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(steps):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    def gemm(i):
+        w_q, w_sf, w_scale = prob.weights[i % len(prob.weights)]
+        moe_fp4.grouped_gemm(prob.q, prob.sf, prob.g, w_q, w_sf, w_scale, prob.off,
+                             a_row_index=prob.idx, out=prob.out, m_total=prob.m_total)
+
+    def quant(i):
+        moe_fp4.quantize(prob.x, tensor_scale=prob.g, q=prob.q, sf=prob.sf, dynamic=True)
+
+    quant_ms = back_to_back(quant)
+    gemm_ms = back_to_back(gemm)
+    return dict(wall_ms_per_step=(t1 - t0) * 1e3 / steps, gpu_ms_per_step=region_ms / steps,
+                quant_ms=quant_ms, gemm_ms=gemm_ms)
 
 
 def plan_of(prob):

@@ -176,40 +176,65 @@ __device__ __forceinline__ ItemLoads<MB, NBW> nowhere(const ItemLoads<MB, NBW>& 
   return z;
 }
 
-// Item i of the work list: the expert owning it is found by binary search in
-// the LDS prefix of item counts; offsets, the row index and the scales are
-// read through the scalar cache, so decoding issues no vector memory access
-// (the vector-memory counter then only tracks the operand stream).
-template <int MB, int NBW, int KSUB>
-__device__ __forceinline__ void decode_item(int32_t i, const int32_t* prefix, const GemmArgs& p,
-                                            int lane, ItemPos& it, ItemLoads<MB, NBW>& ld) {
-  constexpr int BM = 16 * MB;
-  const int c = lane & 15, g = lane >> 4;
-  int lo = 0, hi = p.num_experts;  // prefix[lo] <= i < prefix[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (prefix[mid] <= i) lo = mid; else hi = mid;
+// Work-list tables in LDS, filled once per workgroup: prefix[e] = items of
+// experts before e (prefix[E] = all items) and off[e] = expert offsets clamped
+// into [0, m_total].
+struct WorkList {
+  const int32_t* prefix;
+  const int32_t* off;
+};
+
+// The expert owning item i, searching forward from expert `from` (which owns
+// an item <= i): 64 experts per step, one LDS read and a ballot.  prefix is
+// non-decreasing, so the experts e with prefix[e] <= i form a prefix of the
+// range and their count locates the owner (empty experts are passed over).
+__device__ __forceinline__ int32_t find_expert(int32_t i, int32_t from, const WorkList& wl,
+                                               int32_t E, int lane) {
+  int32_t lo = from;
+  for (;;) {
+    const int32_t e = lo + 1 + lane;
+    const int32_t v = e <= E ? wl.prefix[e] : INT32_MAX;
+    const int32_t t = (int32_t)__popcll(__ballot(v <= i));
+    if (t < 64) return uniform(lo + t);
+    lo += 64;
   }
-  lo = uniform(lo);
-  const int32_t m_total = (int32_t)p.m_total;
-  const sconst_i32 offs = (sconst_i32)p.offsets;
-  const int32_t r_lo = clamp_off(offs[lo], m_total);
-  const int32_t r_hi = clamp_off(offs[lo + 1], m_total);
-  const int32_t cnt = r_hi - r_lo;
+}
+
+// Locate item i (starting the search at expert `from`): LDS reads only, plus
+// the scalar loads of the two tensor scales, which are consumed only by the
+// item's epilogue.
+template <int MB, int NBW>
+__device__ __forceinline__ ItemPos locate_item(int32_t i, int32_t from, const WorkList& wl,
+                                               const GemmArgs& p, int lane) {
+  constexpr int BM = 16 * MB;
+  const int32_t e = find_expert(i, from, wl, p.num_experts, lane);
+  const int32_t r_lo = uniform(wl.off[e]);
+  const int32_t cnt = uniform(wl.off[e + 1]) - r_lo;
   const int32_t mts = (cnt + BM - 1) / BM;
-  const int32_t local = i - uniform(prefix[lo]);
+  const int32_t local = i - uniform(wl.prefix[e]);
   const int32_t nt = local / mts, mt = local - nt * mts;
-  it.e = lo;
+  ItemPos it;
+  it.e = e;
   it.row0 = r_lo + mt * BM;
   const int32_t left = cnt - mt * BM;
   it.rows_valid = left < BM ? left : BM;
   it.n0 = nt * 16 * NBW;
-  it.alpha = ((sconst_f32)p.a_scale)[0] * ((sconst_f32)p.w_scale)[lo];
+  it.alpha = ((sconst_f32)p.a_scale)[0] * ((sconst_f32)p.w_scale)[e];
+  return it;
+}
 
+// The per-lane loads of a located item: this expert's weight resources and
+// each lane's byte offsets.  The 16 row numbers of a row block are read as
+// scalars through the row index, written into lanes 0..15 and spread to every
+// 16-lane group.
+template <int MB, int NBW, int KSUB>
+__device__ __forceinline__ void item_loads(const ItemPos& it, const GemmArgs& p, int lane,
+                                           ItemLoads<MB, NBW>& ld) {
+  const int c = lane & 15, g = lane >> 4;
   // 32-bit offsets: the host guarantees n * k/2 and a_rows * k/2 < 2^31.
   const int32_t n = (int32_t)p.n, kb = (int32_t)(p.k >> 1), nbk = (int32_t)(p.k >> 4);
-  ld.w = make_rsrc(p.w_q + (int64_t)lo * n * kb, (uint32_t)(n * kb));
-  ld.ws = make_rsrc(p.w_sf + (int64_t)lo * n * nbk, (uint32_t)(n * nbk));
+  ld.w = make_rsrc(p.w_q + (int64_t)it.e * n * kb, (uint32_t)(n * kb));
+  ld.ws = make_rsrc(p.w_sf + (int64_t)it.e * n * nbk, (uint32_t)(n * nbk));
   ld.n0 = it.n0;
 #pragma unroll
   for (int jb = 0; jb < NBW; ++jb) {
@@ -229,13 +254,11 @@ __device__ __forceinline__ void decode_item(int32_t i, const int32_t* prefix, co
   const int32_t a_last = (int32_t)p.a_rows - 1;
 #pragma unroll
   for (int ib = 0; ib < MB; ++ib) {
-    // Source row of tile row 16*ib + c.  Rows past the expert's end repeat its
-    // first row: their products are computed and never stored.  The 16 row
-    // numbers are read as scalars, written into lanes 0..15, then spread to
-    // every 16-lane group.
     int32_t src[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
+      // Rows past the expert's end repeat its first row: their products are
+      // computed and never stored.
       const int32_t rr = 16 * ib + j;
       const int32_t r = it.row0 + (rr < it.rows_valid ? rr : 0);
       src[j] = uniform(idx ? idx[r] : r);
@@ -499,9 +522,10 @@ __device__ __forceinline__ void epilogue(float4_t (&acc)[NBW][MB], const ItemPos
   }
 }
 
-// LDS layout: the work-list prefix, then (with SL) each wave's scale buffers.
+// LDS layout: the work-list tables (item prefix and clamped offsets, E+1
+// ints each), then (with SL) each wave's scale buffers.
 __host__ __device__ constexpr size_t prefix_bytes(int num_experts) {
-  return ((size_t)(num_experts + 1) * 4 + 15) / 16 * 16;
+  return ((size_t)(num_experts + 1) * 8 + 15) / 16 * 16;
 }
 
 template <int MB, int NBW, int KSUB, int WAVES, bool SL>
@@ -510,6 +534,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_grouped_gemm(const GemmArgs p) {
   constexpr int NTHR = WAVES * 64;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int32_t* prefix = reinterpret_cast<int32_t*>(smem);  // [num_experts + 1] item prefix
+  int32_t* offl = prefix + (p.num_experts + 1);         // [num_experts + 1] clamped offsets
   __shared__ int32_t wave_sum[WAVES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);  // the compiler cannot see that this is wave-uniform
@@ -539,10 +564,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_grouped_gemm(const GemmArgs p) {
     int32_t run = base + incl - local;
     for (int e = beg; e < end; ++e) {
       prefix[e] = run;
-      const int32_t cnt = clamp_off(p.offsets[e + 1], m_total) - clamp_off(p.offsets[e], m_total);
+      const int32_t lo = clamp_off(p.offsets[e], m_total), hi = clamp_off(p.offsets[e + 1], m_total);
+      offl[e] = lo;
+      const int32_t cnt = hi - lo;  // <= 0 (an empty expert, or a violated precondition): no items
       run += cnt > 0 ? ((cnt + BM - 1) / BM) * p.n_tiles : 0;
     }
-    if (tid == NTHR - 1) prefix[E] = base + incl;
+    if (tid == NTHR - 1) {
+      prefix[E] = base + incl;
+      offl[E] = clamp_off(p.offsets[E], m_total);
+    }
     __syncthreads();
   }
   const int32_t total_items = uniform(prefix[E]);
@@ -597,18 +627,30 @@ __global__ __launch_bounds__(WAVES * 64) void k_grouped_gemm(const GemmArgs p) {
 
   // ld_*: the unit whose loads are issued next; cp: the item being accumulated.
   // Each register stage has its own set of lane offsets (l0 for s0, l1 for s1).
-  ItemPos ld_pos, cp;
+  // nx: the item after ld's, located and with its scalar loads in flight.
+  const WorkList wl{prefix, offl};
+  ItemPos ld_pos, cp, nx;
   ItemLoads<MB, NBW> l0, l1;
   int32_t ld_round = 0, ld_st = 0, cp_round = 0, cp_st = 0;
-  decode_item<MB, NBW, KSUB>(item_of(0), prefix, p, lane, ld_pos, l0);
+  ld_pos = locate_item<MB, NBW>(item_of(0), 0, wl, p, lane);
+  item_loads<MB, NBW, KSUB>(ld_pos, p, lane, l0);
+  // nx: the item after ld's, located a stage or more before it is needed
+  // (the last item repeats itself; that copy is never used).
+  auto locate_next = [&](int32_t round) {
+    const int32_t r = round + 1 < my_items ? round + 1 : round;
+    nx = locate_item<MB, NBW>(item_of(r), ld_pos.e, wl, p, lane);
+  };
+  locate_next(0);
   cp = ld_pos;
-  // Move the load position to the next unit: a new item is decoded into dst,
-  // otherwise dst takes src's offsets.
+  // Move the load position to the next unit: a new item (already located)
+  // gets its lane offsets in dst, otherwise dst takes src's offsets.
   auto advance = [&](ItemLoads<MB, NBW>& dst, const ItemLoads<MB, NBW>& src) {
     if (++ld_st == nst) {
       ld_st = 0;
       ++ld_round;
-      decode_item<MB, NBW, KSUB>(item_of(ld_round), prefix, p, lane, ld_pos, dst);
+      ld_pos = nx;
+      item_loads<MB, NBW, KSUB>(ld_pos, p, lane, dst);
+      locate_next(ld_round);
     } else {
       dst = src;
     }
