@@ -47,33 +47,16 @@
 #include <tuple>
 
 #include "fp4_device.h"
+#include "gemm_common.h"
 #include "launch.h"
 
 namespace moe_fp4 {
 namespace {
 
-constexpr int kXcds = 8;
-// Word 3 of a raw buffer resource on gfx9-class GPUs: 32-bit data format,
-// no swizzle, range checking on (an access at or past num_records reads 0 and
-// a store there is dropped).
-constexpr int kRawBufferWord3 = 0x00020000;
-// A buffer offset past every resource built here (each covers < 2^31 bytes).
-constexpr uint32_t kOutOfRange = 0x80000000u;
 // K elements whose block scales fill one 128-byte line of a row.
 constexpr int kSpan = 2048;
 
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-// Pointers the compiler reads through the scalar cache (uniform addresses).
-typedef const int32_t __attribute__((address_space(4)))* sconst_i32;
-typedef const float __attribute__((address_space(4)))* sconst_f32;
 typedef __attribute__((address_space(3))) void* lds_ptr;
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           kRawBufferWord3);
-}
-
-__device__ __forceinline__ int32_t uniform(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // v_writelane_b32: lane J of `v` takes the wavefront-uniform value `s`.
 template <int J>
@@ -86,23 +69,6 @@ template <int J>
 __device__ __forceinline__ int32_t gather16(int32_t v, const int32_t (&s)[16]) {
   if constexpr (J < 16) return gather16<J + 1>(write_lane<J>(v, s[J]), s);
   else return v;
-}
-
-__device__ __forceinline__ int32_t clamp_off(int32_t v, int32_t m_total) {
-  return v < 0 ? 0 : (v > m_total ? m_total : v);
-}
-
-// Logical number of workgroup b in a grid of nblk (a multiple of 8) when only
-// the first `active` logical workgroups have work: those are split evenly over
-// the 8 XCDs (workgroup b runs on XCD b % 8), consecutive logical numbers on
-// one XCD; the rest follow.  A bijection of [0, nblk).
-__device__ __forceinline__ int logical_block(int b, int nblk, int active) {
-  const int per_xcd = nblk / kXcds;
-  int pxa = (active + kXcds - 1) / kXcds;
-  pxa = pxa < per_xcd ? pxa : per_xcd;
-  const int xcd = b % kXcds, slot = b / kXcds;
-  if (slot < pxa) return xcd * pxa + slot;
-  return kXcds * pxa + xcd * (per_xcd - pxa) + (slot - pxa);
 }
 
 // LDS bytes per wave for staged weight scales: two span buffers of 16*NBW
@@ -127,15 +93,6 @@ struct Stage {
   uint32_t ws[NBW][KSUB];
   u32x4_t a[MB][KSUB][2];
   uint32_t as[MB][KSUB];
-};
-
-// Where a work item lives; every field is wavefront-uniform.
-struct ItemPos {
-  int32_t e;
-  int32_t rows_valid;  // rows of this M-tile that belong to the expert (1..16*MB)
-  int32_t row0;        // first output row of the M-tile
-  int32_t n0;          // first output column of the N-tile
-  float alpha;         // a_scale * w_scale[e]
 };
 
 // The loads of a work item: this expert's weight resources and each lane's
@@ -174,53 +131,6 @@ __device__ __forceinline__ ItemLoads<MB, NBW> nowhere(const ItemLoads<MB, NBW>& 
   z.sl_voff = kOutOfRange;
   z.n0 = 0x40000000;  // no scale-line copy either
   return z;
-}
-
-// Work-list tables in LDS, filled once per workgroup: prefix[e] = items of
-// experts before e (prefix[E] = all items) and off[e] = expert offsets clamped
-// into [0, m_total].
-struct WorkList {
-  const int32_t* prefix;
-  const int32_t* off;
-};
-
-// The expert owning item i, searching forward from expert `from` (which owns
-// an item <= i): 64 experts per step, one LDS read and a ballot.  prefix is
-// non-decreasing, so the experts e with prefix[e] <= i form a prefix of the
-// range and their count locates the owner (empty experts are passed over).
-__device__ __forceinline__ int32_t find_expert(int32_t i, int32_t from, const WorkList& wl,
-                                               int32_t E, int lane) {
-  int32_t lo = from;
-  for (;;) {
-    const int32_t e = lo + 1 + lane;
-    const int32_t v = e <= E ? wl.prefix[e] : INT32_MAX;
-    const int32_t t = (int32_t)__popcll(__ballot(v <= i));
-    if (t < 64) return uniform(lo + t);
-    lo += 64;
-  }
-}
-
-// Locate item i (starting the search at expert `from`): LDS reads only, plus
-// the scalar loads of the two tensor scales, which are consumed only by the
-// item's epilogue.
-template <int MB, int NBW>
-__device__ __forceinline__ ItemPos locate_item(int32_t i, int32_t from, const WorkList& wl,
-                                               const GemmArgs& p, int lane) {
-  constexpr int BM = 16 * MB;
-  const int32_t e = find_expert(i, from, wl, p.num_experts, lane);
-  const int32_t r_lo = uniform(wl.off[e]);
-  const int32_t cnt = uniform(wl.off[e + 1]) - r_lo;
-  const int32_t mts = (cnt + BM - 1) / BM;
-  const int32_t local = i - uniform(wl.prefix[e]);
-  const int32_t nt = local / mts, mt = local - nt * mts;
-  ItemPos it;
-  it.e = e;
-  it.row0 = r_lo + mt * BM;
-  const int32_t left = cnt - mt * BM;
-  it.rows_valid = left < BM ? left : BM;
-  it.n0 = nt * 16 * NBW;
-  it.alpha = ((sconst_f32)p.a_scale)[0] * ((sconst_f32)p.w_scale)[e];
-  return it;
 }
 
 // The per-lane loads of a located item: this expert's weight resources and
@@ -522,12 +432,6 @@ __device__ __forceinline__ void epilogue(float4_t (&acc)[NBW][MB], const ItemPos
   }
 }
 
-// LDS layout: the work-list tables (item prefix and clamped offsets, E+1
-// ints each), then (with SL) each wave's scale buffers.
-__host__ __device__ constexpr size_t prefix_bytes(int num_experts) {
-  return ((size_t)(num_experts + 1) * 8 + 15) / 16 * 16;
-}
-
 template <int MB, int NBW, int KSUB, int WAVES, bool SL>
 __global__ __launch_bounds__(WAVES * 64) void k_grouped_gemm(const GemmArgs p) {
   constexpr int BM = 16 * MB;
@@ -541,41 +445,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_grouped_gemm(const GemmArgs p) {
   const int E = p.num_experts;
   const int32_t m_total = (int32_t)p.m_total;
 
-  // ---- work list: exclusive prefix over experts of (M-tiles * N-tiles) ----
-  {
-    const int per = (E + NTHR - 1) / NTHR;
-    const int beg = tid * per < E ? tid * per : E;
-    const int end = beg + per < E ? beg + per : E;
-    int32_t local = 0;
-    for (int e = beg; e < end; ++e) {
-      const int32_t cnt = clamp_off(p.offsets[e + 1], m_total) - clamp_off(p.offsets[e], m_total);
-      local += cnt > 0 ? ((cnt + BM - 1) / BM) * p.n_tiles : 0;
-    }
-    int32_t incl = local;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int32_t t = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += t;
-    }
-    if (lane == 63) wave_sum[wave] = incl;
-    __syncthreads();
-    int32_t base = 0;
-    for (int w = 0; w < wave; ++w) base += wave_sum[w];
-    int32_t run = base + incl - local;
-    for (int e = beg; e < end; ++e) {
-      prefix[e] = run;
-      const int32_t lo = clamp_off(p.offsets[e], m_total), hi = clamp_off(p.offsets[e + 1], m_total);
-      offl[e] = lo;
-      const int32_t cnt = hi - lo;  // <= 0 (an empty expert, or a violated precondition): no items
-      run += cnt > 0 ? ((cnt + BM - 1) / BM) * p.n_tiles : 0;
-    }
-    if (tid == NTHR - 1) {
-      prefix[E] = base + incl;
-      offl[E] = clamp_off(p.offsets[E], m_total);
-    }
-    __syncthreads();
-  }
-  const int32_t total_items = uniform(prefix[E]);
+  const int32_t total_items = build_worklist<NTHR>(p, BM, prefix, offl, wave_sum);
+
 
   // ---- XCD-aware wavefront numbering ----
   // Items are dealt in rounds of nw (one per wavefront).  Within a round, the
@@ -607,7 +478,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_grouped_gemm(const GemmArgs p) {
   // This wave's scale-line buffers (SL): span buffers 0 and 1, then the sink.
   constexpr int kSpanStages = kSpan / (256 * KSUB);  // stages per span
   constexpr int kBufBytes = 16 * NBW * 128;
-  uint8_t* const sl_base = smem + prefix_bytes(E) + (size_t)wave * scale_lds_per_wave<NBW>();
+  uint8_t* const sl_base = smem + worklist_bytes(E) + (size_t)wave * scale_lds_per_wave<NBW>();
   auto line_copy = [&](int32_t round, int32_t st) -> LineCopy {
     LineCopy lc;
     const bool start = st % kSpanStages == 0;
@@ -632,13 +503,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_grouped_gemm(const GemmArgs p) {
   ItemPos ld_pos, cp, nx;
   ItemLoads<MB, NBW> l0, l1;
   int32_t ld_round = 0, ld_st = 0, cp_round = 0, cp_st = 0;
-  ld_pos = locate_item<MB, NBW>(item_of(0), 0, wl, p, lane);
+  ld_pos = locate(item_of(0), 0, wl, p, 16 * MB, 16 * NBW, lane);
   item_loads<MB, NBW, KSUB>(ld_pos, p, lane, l0);
   // nx: the item after ld's, located a stage or more before it is needed
   // (the last item repeats itself; that copy is never used).
   auto locate_next = [&](int32_t round) {
     const int32_t r = round + 1 < my_items ? round + 1 : round;
-    nx = locate_item<MB, NBW>(item_of(r), ld_pos.e, wl, p, lane);
+    nx = locate(item_of(r), ld_pos.e, wl, p, 16 * MB, 16 * NBW, lane);
   };
   locate_next(0);
   cp = ld_pos;
@@ -724,30 +595,19 @@ __global__ __launch_bounds__(WAVES * 64) void k_grouped_gemm(const GemmArgs p) {
   }
 }
 
-// Resident workgroups the device can hold for one kernel, queried once per
-// (device, kernel, LDS size) and kept: the query costs more host time than a
-// small decode GEMM takes on the GPU.
-struct ResidentCache {
-  std::mutex mu;
-  std::map<std::tuple<int, const void*, size_t>, int> groups;
-};
+}  // namespace
 
-inline ResidentCache& resident_cache() {
-  static ResidentCache c;
-  return c;
-}
-
-template <typename K>
-hipError_t resident_groups(K kern, int threads, size_t lds, int* out) {
+hipError_t resident_groups_of(const void* kern, int threads, size_t lds, int* out) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, const void*, size_t>, int> groups;
   int dev = 0;
   hipError_t err = hipGetDevice(&dev);
   if (err != hipSuccess) return err;
-  const auto key = std::make_tuple(dev, reinterpret_cast<const void*>(kern), lds);
-  ResidentCache& c = resident_cache();
+  const auto key = std::make_tuple(dev, kern, lds);
   {
-    std::lock_guard<std::mutex> g(c.mu);
-    auto it = c.groups.find(key);
-    if (it != c.groups.end()) {
+    std::lock_guard<std::mutex> g(mu);
+    auto it = groups.find(key);
+    if (it != groups.end()) {
       *out = it->second;
       return hipSuccess;
     }
@@ -759,16 +619,18 @@ hipError_t resident_groups(K kern, int threads, size_t lds, int* out) {
   err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, lds);
   if (err != hipSuccess) return err;
   if (per_cu < 1) per_cu = 1;
-  std::lock_guard<std::mutex> g(c.mu);
-  c.groups[key] = cus * per_cu;
+  std::lock_guard<std::mutex> g(mu);
+  groups[key] = cus * per_cu;
   *out = cus * per_cu;
   return hipSuccess;
 }
 
+namespace {
+
 template <int MB, int NBW, int KSUB, int WAVES, bool SL>
 hipError_t launch_tile(const GemmArgs& p, hipStream_t stream) {
   auto kern = k_grouped_gemm<MB, NBW, KSUB, WAVES, SL>;
-  const size_t lds = prefix_bytes(p.num_experts) + (SL ? (size_t)WAVES * scale_lds_per_wave<NBW>() : 0);
+  const size_t lds = worklist_bytes(p.num_experts) + (SL ? (size_t)WAVES * scale_lds_per_wave<NBW>() : 0);
   int resident = 0;
   hipError_t err = resident_groups(kern, WAVES * 64, lds, &resident);
   if (err != hipSuccess) return err;
@@ -789,10 +651,12 @@ hipError_t launch_tile(const GemmArgs& p, hipStream_t stream) {
 
 GemmTile choose_tile(int32_t num_experts, int64_t m_total, int64_t n, int64_t k, const char* env) {
   (void)n;
-  GemmTile t{1, 4, 4, 1, 0};
+  GemmTile t{1, 4, 4, 1, 0, 0};
   const int64_t avg = num_experts > 0 ? (m_total + num_experts - 1) / num_experts : m_total;
   if (avg > 32) t.m_blocks = 4;
   else if (avg > 16) t.m_blocks = 2;
+  // Experts this large are compute-bound: share dequantised operands in LDS.
+  if (avg >= 96) t = GemmTile{8, 8, 4, 1, 0, 1};
   if (k % 512 == 0) t.k_sub = 2;
   t.lds_scales = k % kSpan == 0 ? 1 : 0;
   if (env && *env) {
@@ -813,11 +677,18 @@ GemmTile choose_tile(int32_t num_experts, int64_t m_total, int64_t n, int64_t k,
     const bool regs = ok && *s == 'r';
     if (regs) ++s;
     ok = ok && *s == '\0' && nv >= 2;
+    if (ok && nv == 2 && v[0] == 128 && v[1] == 128 && !regs) {
+      t = GemmTile{8, 8, 4, 1, 0, 1};
+      return t;
+    }
     ok = ok && (v[0] == 16 || v[0] == 32 || v[0] == 64) && (v[1] == 32 || v[1] == 64);
     if (nv == 3)
       ok = ok && (v[2] == 256 || (v[2] == 512 && k % 512 == 0) ||
                   (v[2] == 1024 && k % 1024 == 0 && v[1] == 32 && v[0] <= 32));
     if (ok) {
+      t.tiled = 0;
+      t.lds_scales = k % kSpan == 0 ? 1 : 0;
+      t.k_sub = k % 512 == 0 ? 2 : 1;
       t.m_blocks = v[0] / 16;
       t.n_blocks = v[1] / 16;
       if (nv == 3) t.k_sub = v[2] / 256;
@@ -828,7 +699,8 @@ GemmTile choose_tile(int32_t num_experts, int64_t m_total, int64_t n, int64_t k,
 }
 
 int64_t gemm_lds_bytes(const GemmTile& t, int32_t num_experts) {
-  int64_t b = (int64_t)prefix_bytes(num_experts) + (int64_t)sizeof(int32_t) * t.waves;
+  if (t.tiled) return (int64_t)tiled_lds(num_experts) + 16;
+  int64_t b = (int64_t)worklist_bytes(num_experts) + (int64_t)sizeof(int32_t) * t.waves;
   if (t.lds_scales) b += (int64_t)t.waves * (2 * 16 * 16 * t.n_blocks * 8 + 1024);
   return b;
 }
@@ -869,6 +741,7 @@ hipError_t launch_sl(const GemmArgs& p, const GemmTile& t, hipStream_t stream) {
 }
 
 hipError_t launch_grouped_gemm(const GemmArgs& p, const GemmTile& t, hipStream_t stream) {
+  if (t.tiled) return launch_grouped_gemm_tiled(p, stream);
   if (t.waves != 4 || p.k % (256 * t.k_sub) != 0) return hipErrorInvalidValue;
   if (t.lds_scales) {
     if (p.k % kSpan != 0) return hipErrorInvalidValue;

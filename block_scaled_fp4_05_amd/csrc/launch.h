@@ -22,6 +22,7 @@ struct GemmTile {
   int waves;
   int k_sub;
   int lds_scales;  // weight block scales staged through LDS (needs k % 2048 == 0)
+  int tiled;       // workgroup-tiled kernel (128 x 128 items, operands shared in LDS)
 };
 
 constexpr int kKStep = 256;  // K granularity the kernels require
@@ -55,5 +56,9 @@ struct GemmArgs {
 };
 
 hipError_t launch_grouped_gemm(const GemmArgs& args, const GemmTile& tile, hipStream_t stream);
+
+// Workgroup-tiled kernel (grouped_gemm_tiled.hip): 128 x 128 items, 4 waves.
+hipError_t launch_grouped_gemm_tiled(const GemmArgs& args, hipStream_t stream);
+size_t tiled_lds(int32_t num_experts);
 
 }  // namespace moe_fp4

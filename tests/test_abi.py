@@ -54,10 +54,15 @@ def test_plan_picks_tiles_by_rows_per_expert(monkeypatch):
     monkeypatch.delenv("MOE_FP4_TILE", raising=False)
     assert m.plan(256, 4096, 512, 6144)["tile_m"] == 16
     assert m.plan(256, 8192, 6144, 256)["tile_m"] == 32
-    assert m.plan(1, 8192, 8192, 8192)["tile_m"] == 64
+    assert m.plan(1, 8192, 8192, 8192)["tile_m"] == 128   # compute-bound: workgroup tile
+    assert m.plan(256, 32768, 512, 6144)["tile_m"] == 128
+    assert m.plan(256, 16384, 512, 6144)["tile_m"] == 64
     monkeypatch.setenv("MOE_FP4_TILE", "64x32")
     p = m.plan(256, 4096, 512, 6144)
     assert (p["tile_m"], p["tile_n"]) == (64, 32)
+    monkeypatch.setenv("MOE_FP4_TILE", "128x128")
+    p = m.plan(256, 4096, 512, 6144)
+    assert (p["tile_m"], p["tile_n"], p["k_step"]) == (128, 128, 64)
     monkeypatch.setenv("MOE_FP4_TILE", "48x64")  # unsupported -> ignored
     assert m.plan(256, 4096, 512, 6144)["tile_m"] == 16
 

@@ -79,7 +79,7 @@ def _check_rows(got_bits, P, rows_sel=None, a_row_index=None, label=""):
     return float(err.max()) if err.size else 0.0
 
 
-TILES = ["16x64", "32x64", "64x64", "16x32", "32x32", "64x32"]
+TILES = ["16x64", "32x64", "64x64", "16x32", "32x32", "64x32", "128x128"]
 
 
 @pytest.mark.parametrize("tile", TILES)
