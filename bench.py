@@ -7,6 +7,9 @@ One step = the whole path over one batch of synthetic decode input:
   2. moe_grouped_gemm_fp4: every expert's GEMM over the tokens routed to it
      (rows gathered through a row index), FP32 accumulation, BF16 output.
 Both run in the HIP library; inputs are resident in HBM before timing starts.
+The expert weights are constant, so they are rearranged once at set-up into the
+packed layout the GEMM loads fastest (moe_fp4_pack_weights, untimed; its own
+duration is reported); --layout rowmajor times the GEMM on row-major weights.
 
 Weights are rotated over several device copies so that each step streams
 weights that neither the L2 nor the 256 MB Infinity Cache holds (the decode
@@ -57,6 +60,8 @@ def parse_args():
     ap.add_argument("--workload", default="c3", help="c1, c2, c3, c4, c5 or c5b (default c3)")
     ap.add_argument("--secondary", default="c4",
                     help="second workload reported in the same line ('none' to skip)")
+    ap.add_argument("--layout", default="packed", choices=("packed", "rowmajor"),
+                    help="weight-code layout the GEMM reads (default packed)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a device copy of known size (counter scale factor)")
@@ -90,7 +95,7 @@ class Problem:
     """Device-resident inputs of one workload (weights quantised on the GPU by
     moe_fp4_quantize from the seeded FP32 weights)."""
 
-    def __init__(self, name, keep_host_weights=False):
+    def __init__(self, name, keep_host_weights=False, layout="packed"):
         import numpy as np
         import torch
         from block_scaled_fp4_05_amd import moe_fp4
@@ -121,6 +126,20 @@ class Problem:
             moe_fp4.quantize(wt, tensor_scale=w_scale[e:e + 1], q=w_q[e], sf=w_sf[e], dynamic=True)
         torch.cuda.synchronize()
         log(f"{name}: weights quantised on the GPU in {time.time() - t0:.1f}s")
+        self.packed = layout == "packed"
+        self.pack_us = None
+        if self.packed:
+            w_pk = torch.empty_like(w_q)
+            moe_fp4.pack_weights(w_q, out=w_pk)  # first call loads the kernel
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            moe_fp4.pack_weights(w_q, out=w_pk)
+            e1.record()
+            torch.cuda.synchronize()
+            self.pack_us = round(e0.elapsed_time(e1) * 1e3, 1)
+            del w_q
+            w_q = w_pk
         wbytes = E * n * k * (0.5 + 1.0 / 16.0)
         copies = max(1, min(8, math.ceil(ROTATE_BYTES / wbytes)))
         self.weights = [(w_q, w_sf, w_scale)]
@@ -135,18 +154,15 @@ class Problem:
         self.quant_bytes = quant_alg_bytes(w.tokens, k)
         torch.cuda.synchronize()
 
-    def step(self, i, ev=None):
+    def step(self, i):
+        """One pass of the hot path: quantise the step's activations, then the
+        grouped GEMM over every expert (weights rotated by step)."""
         from block_scaled_fp4_05_amd import moe_fp4
         w_q, w_sf, w_scale = self.weights[i % len(self.weights)]
-        if ev is not None:
-            ev[0].record()
         moe_fp4.quantize(self.x, tensor_scale=self.g, q=self.q, sf=self.sf, dynamic=True)
-        if ev is not None:
-            ev[1].record()
         moe_fp4.grouped_gemm(self.q, self.sf, self.g, w_q, w_sf, w_scale, self.off,
-                             a_row_index=self.idx, out=self.out, m_total=self.m_total)
-        if ev is not None:
-            ev[2].record()
+                             a_row_index=self.idx, out=self.out, m_total=self.m_total,
+                             packed=self.packed)
 
 
 def measure(prob, steps, warmup):
@@ -186,7 +202,8 @@ def measure(prob, steps, warmup):
     def gemm(i):
         w_q, w_sf, w_scale = prob.weights[i % len(prob.weights)]
         moe_fp4.grouped_gemm(prob.q, prob.sf, prob.g, w_q, w_sf, w_scale, prob.off,
-                             a_row_index=prob.idx, out=prob.out, m_total=prob.m_total)
+                             a_row_index=prob.idx, out=prob.out, m_total=prob.m_total,
+                             packed=prob.packed)
 
     def quant(i):
         moe_fp4.quantize(prob.x, tensor_scale=prob.g, q=prob.q, sf=prob.sf, dynamic=True)
@@ -219,6 +236,8 @@ def summary(prob, r):
         gemm_fp4_peak_frac=round(prob.flops / gemm_s / 1e12 / FP4_PEAK_TFLOPS, 5),
         gemm_f16_mfma_peak_frac=round(prob.flops / gemm_s / 1e12 / F16_PEAK_TFLOPS, 5),
         tile=plan_of(prob),
+        weight_layout="packed" if prob.packed else "rowmajor",
+        weight_pack_us=prob.pack_us,
         weight_copies_rotated=len(prob.weights),
     )
 
@@ -233,9 +252,10 @@ def sources_digest():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, layout):
     """HBM bytes per grouped-GEMM launch from the committed counter summary, or None
-    when it is missing, for another workload, or taken on other kernel sources."""
+    when it is missing, for another workload or weight layout, or taken on other
+    kernel sources."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     vals = {}
@@ -245,7 +265,8 @@ def measured_traffic(workload):
                 key, v = line.split(":", 1)
                 vals[key.strip()] = v.strip()
     try:
-        if vals.get("workload") != workload or vals.get("sources_sha256_16") != sources_digest():
+        if (vals.get("workload") != workload or vals.get("layout", "rowmajor") != layout
+                or vals.get("sources_sha256_16") != sources_digest()):
             return None
         return float(vals["hbm_bytes_per_dispatch"])
     except (KeyError, ValueError):
@@ -324,7 +345,7 @@ def main():
         return
 
     want_cpu = not args.no_cpu_baseline
-    prob = Problem(args.workload, keep_host_weights=want_cpu)
+    prob = Problem(args.workload, keep_host_weights=want_cpu, layout=args.layout)
     log(f"{args.workload}: {args.warmup} warmup + {args.steps} timed steps")
     r = measure(prob, args.steps, args.warmup)
     main_s = summary(prob, r)
@@ -332,7 +353,7 @@ def main():
 
     gemm_s = r["gemm_ms"] * 1e-3
     achieved = prob.gemm_bytes / gemm_s / 1e9
-    traffic = measured_traffic(args.workload)
+    traffic = measured_traffic(args.workload, args.layout)
     roof = {"bound": "hbm", "kernel": "k_grouped_gemm", "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic, "algorithmic_bytes": int(prob.gemm_bytes),
@@ -340,7 +361,7 @@ def main():
 
     secondary = None
     if args.secondary and args.secondary != "none" and args.secondary != args.workload:
-        p2 = Problem(args.secondary)
+        p2 = Problem(args.secondary, layout=args.layout)
         r2 = measure(p2, args.steps, args.warmup)
         secondary = summary(p2, r2)
         log(json.dumps(secondary))

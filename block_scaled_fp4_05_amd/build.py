@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_fp4.so")
-SOURCES = ["api.cpp", "quantize.hip", "grouped_gemm.hip", "grouped_gemm_tiled.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "grouped_gemm.hip", "grouped_gemm_tiled.hip", "pack.hip"]
 HEADERS = ["fp4_device.h", "gemm_common.h", "launch.h"]
 
 HIPCC_FLAGS = [
@@ -30,16 +30,36 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Always recompiles; writes the library atomically."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"),
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
-    if verbose:
-        print(res.stderr)
-    os.replace(tmp, LIB)
+    """Always recompiles (each source to an object in parallel, then one link);
+    writes the library atomically."""
+    from concurrent.futures import ThreadPoolExecutor
+    import tempfile
+
+    cc = hipcc()
+    inc = ["-I", os.path.join(ROOT, "include")]
+    with tempfile.TemporaryDirectory(prefix="moe_fp4_build_") as tmpdir:
+        def compile_one(src):
+            obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
+            cmd = [cc, *[f for f in HIPCC_FLAGS if f != "-shared"], *inc, "-c",
+                   os.path.join(CSRC, src), "-o", obj]
+            return obj, subprocess.run(cmd, capture_output=True, text=True)
+
+        workers = max(1, min(len(SOURCES), os.cpu_count() or 1, 8))
+        with ThreadPoolExecutor(max_workers=workers) as pool:
+            results = list(pool.map(compile_one, SOURCES))
+        log = []
+        for (obj, res), src in zip(results, SOURCES):
+            log.append(res.stdout + res.stderr)
+            if res.returncode != 0:
+                raise RuntimeError(f"hipcc failed on {src}:\n" + res.stdout + res.stderr)
+        tmp = LIB + ".tmp%d" % os.getpid()
+        link = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", *[o for o, _ in results], "-o", tmp]
+        res = subprocess.run(link, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("link failed:\n" + res.stdout + res.stderr)
+        if verbose:
+            print("".join(log) + res.stderr)
+        os.replace(tmp, LIB)
     return LIB
 
 

@@ -18,7 +18,7 @@ using moe_fp4::GemmTile;
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 constexpr int32_t kMaxExperts = 16384;  // the work-list prefix lives in LDS
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -53,7 +53,7 @@ const char* moe_fp4_status_string(int status) {
     case MOE_FP4_ERR_ALIGN: return "a pointer or leading dimension is misaligned";
     case MOE_FP4_ERR_UNSUPPORTED: return "valid arguments outside what the kernels support";
     case MOE_FP4_ERR_HIP: return "the HIP runtime reported an error";
-    case MOE_FP4_ERR_ARG: return "an enumerated argument has an unknown value";
+    case MOE_FP4_ERR_ARG: return "an enumerated argument has an unknown value, or buffers overlap";
     default: return "unknown status";
   }
 }
@@ -101,12 +101,15 @@ int moe_grouped_gemm_fp4_plan(int32_t num_experts, int64_t m_total, int64_t n, i
   return MOE_FP4_OK;
 }
 
-int moe_grouped_gemm_fp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a_scale,
-                         int64_t a_rows, const int32_t* a_row_index,
-                         const uint8_t* w_q, const uint8_t* w_sf, const float* w_scale,
-                         const int32_t* expert_offsets, int32_t num_experts,
-                         int64_t m_total, int64_t n, int64_t k,
-                         uint16_t* out, int64_t ldo, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const float* a_scale, int64_t a_rows,
+                 const int32_t* a_row_index, const uint8_t* w_q, const uint8_t* w_sf,
+                 const float* w_scale, const int32_t* expert_offsets, int32_t num_experts,
+                 int64_t m_total, int64_t n, int64_t k, uint16_t* out, int64_t ldo,
+                 void* stream, bool packed) {
   if (!a_q || !a_sf || !a_scale || !w_q || !w_sf || !w_scale || !expert_offsets || !out)
     return MOE_FP4_ERR_NULL;
   if (num_experts < 1 || m_total < 0 || n < 1 || k < 1 || ldo < n || a_rows < 0)
@@ -123,8 +126,12 @@ int moe_grouped_gemm_fp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a
   // offsets as well.
   if (a_rows * (k / 2) > (int64_t)INT32_MAX - 4096 || ldo > (1 << 23))
     return MOE_FP4_ERR_UNSUPPORTED;
-  if (m_total == 0) return MOE_FP4_OK;
   const GemmTile t = moe_fp4::choose_tile(num_experts, m_total, n, k, getenv("MOE_FP4_TILE"));
+  // Packed weights fix the per-wavefront K step to the layout's granule.
+  if (packed && !t.tiled &&
+      (t.n_blocks != 4 || t.k_sub != moe_fp4::packed_granule(k) / moe_fp4::kKStep))
+    return MOE_FP4_ERR_UNSUPPORTED;
+  if (m_total == 0) return MOE_FP4_OK;
   GemmArgs p;
   p.a_q = a_q;
   p.a_sf = a_sf;
@@ -142,8 +149,58 @@ int moe_grouped_gemm_fp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a
   p.ldo = ldo;
   p.num_experts = num_experts;
   p.n_tiles = (int32_t)((n + 16 * t.n_blocks - 1) / (16 * t.n_blocks));
+  p.w_packed = packed ? 1 : 0;
   hipError_t err = moe_fp4::launch_grouped_gemm(p, t, reinterpret_cast<hipStream_t>(stream));
   return err == hipSuccess ? MOE_FP4_OK : MOE_FP4_ERR_HIP;
+}
+
+int repack(const uint8_t* src, uint8_t* dst, int32_t num_experts, int64_t n, int64_t k,
+           void* stream, bool to_packed) {
+  if (!src || !dst) return MOE_FP4_ERR_NULL;
+  if (num_experts < 1 || n < 1 || k < 1) return MOE_FP4_ERR_SHAPE;
+  if (n % 16 != 0 || k % moe_fp4::kKStep != 0) return MOE_FP4_ERR_UNSUPPORTED;
+  if (n > INT32_MAX / 2 || n * (k / 2) > (int64_t)INT32_MAX - 4096) return MOE_FP4_ERR_UNSUPPORTED;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return MOE_FP4_ERR_ALIGN;
+  const uintptr_t bytes = (uintptr_t)num_experts * (uintptr_t)n * (uintptr_t)(k / 2);
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  if (a < b + bytes && b < a + bytes) return MOE_FP4_ERR_ARG;  // overlapping buffers
+  hipError_t err = moe_fp4::launch_repack(src, dst, num_experts, n, k, to_packed,
+                                          reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? MOE_FP4_OK : MOE_FP4_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_grouped_gemm_fp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a_scale,
+                         int64_t a_rows, const int32_t* a_row_index,
+                         const uint8_t* w_q, const uint8_t* w_sf, const float* w_scale,
+                         const int32_t* expert_offsets, int32_t num_experts,
+                         int64_t m_total, int64_t n, int64_t k,
+                         uint16_t* out, int64_t ldo, void* stream) {
+  return grouped_gemm(a_q, a_sf, a_scale, a_rows, a_row_index, w_q, w_sf, w_scale,
+                      expert_offsets, num_experts, m_total, n, k, out, ldo, stream, false);
+}
+
+int moe_grouped_gemm_fp4_packed(const uint8_t* a_q, const uint8_t* a_sf, const float* a_scale,
+                                int64_t a_rows, const int32_t* a_row_index,
+                                const uint8_t* w_packed, const uint8_t* w_sf,
+                                const float* w_scale, const int32_t* expert_offsets,
+                                int32_t num_experts, int64_t m_total, int64_t n, int64_t k,
+                                uint16_t* out, int64_t ldo, void* stream) {
+  return grouped_gemm(a_q, a_sf, a_scale, a_rows, a_row_index, w_packed, w_sf, w_scale,
+                      expert_offsets, num_experts, m_total, n, k, out, ldo, stream, true);
+}
+
+int moe_fp4_pack_weights(const uint8_t* w_q, uint8_t* w_packed, int32_t num_experts,
+                         int64_t n, int64_t k, void* stream) {
+  return repack(w_q, w_packed, num_experts, n, k, stream, true);
+}
+
+int moe_fp4_unpack_weights(const uint8_t* w_packed, uint8_t* w_q, int32_t num_experts,
+                           int64_t n, int64_t k, void* stream) {
+  return repack(w_packed, w_q, num_experts, n, k, stream, false);
 }
 
 }  // extern "C"

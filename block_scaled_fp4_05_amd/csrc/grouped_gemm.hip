@@ -137,7 +137,7 @@ __device__ __forceinline__ ItemLoads<MB, NBW> nowhere(const ItemLoads<MB, NBW>& 
 // each lane's byte offsets.  The 16 row numbers of a row block are read as
 // scalars through the row index, written into lanes 0..15 and spread to every
 // 16-lane group.
-template <int MB, int NBW, int KSUB>
+template <int MB, int NBW, int KSUB, bool PK>
 __device__ __forceinline__ void item_loads(const ItemPos& it, const GemmArgs& p, int lane,
                                            ItemLoads<MB, NBW>& ld) {
   const int c = lane & 15, g = lane >> 4;
@@ -146,11 +146,15 @@ __device__ __forceinline__ void item_loads(const ItemPos& it, const GemmArgs& p,
   ld.w = make_rsrc(p.w_q + (int64_t)it.e * n * kb, (uint32_t)(n * kb));
   ld.ws = make_rsrc(p.w_sf + (int64_t)it.e * n * nbk, (uint32_t)(n * nbk));
   ld.n0 = it.n0;
+  // Packed codes (PK, 64-column items): the item is one 64-row group; block
+  // jb of a stage holds rows 16*jb .. +15 in this kernel's lane order.
+  constexpr int32_t kBlock = 16 * 128 * KSUB;
 #pragma unroll
   for (int jb = 0; jb < NBW; ++jb) {
     const int32_t row = it.n0 + 16 * jb + c;
     const bool ok = row < n;
-    ld.w_voff[jb] = ok ? (uint32_t)(row * kb + 32 * KSUB * g) : kOutOfRange;
+    const int32_t wv = PK ? it.n0 * kb + jb * kBlock + 16 * lane : row * kb + 32 * KSUB * g;
+    ld.w_voff[jb] = ok ? (uint32_t)wv : kOutOfRange;
     ld.ws_voff[jb] = ok ? (uint32_t)(row * nbk + 4 * KSUB * g) : kOutOfRange;
   }
   // Scale-line copies move 8 rows x 128 bytes per instruction: lane l takes
@@ -215,10 +219,15 @@ struct LineCopy {
 // in-flight load still reads.  With SL, the stage first copies the 128-byte
 // scale lines of the item's 16*NBW weight rows for its span into LDS, or, if
 // it starts no span, issues the same copies out of range into the sink.
-template <int MB, int NBW, int KSUB, bool SL>
+template <int MB, int NBW, int KSUB, bool SL, bool PK>
 __device__ __forceinline__ void issue_loads(Stage<MB, NBW, KSUB>& st, const ItemLoads<MB, NBW>& it,
                                             const rsrc_t& a_rs, const rsrc_t& as_rs, int32_t kst,
                                             const LineCopy& lc, int32_t n, int32_t nbk) {
+  // Packed codes: a stage is granule kst of the item's 64-row group, rg blocks
+  // of 16 rows one after another (rg < 4 only in a last, partial group).
+  constexpr int32_t kBlock = 16 * 128 * KSUB;
+  const int32_t left = (n - it.n0) >> 4;
+  const int32_t wk = PK ? (left < NBW ? left : NBW) * kBlock : 0;
   if constexpr (SL) {
     const bool on = lc.span >= 0;
     const int32_t soff = uniform(on ? lc.span * 128 : 0);
@@ -232,12 +241,17 @@ __device__ __forceinline__ void issue_loads(Stage<MB, NBW, KSUB>& st, const Item
     }
   }
   const int32_t qk = uniform(kst * 128 * KSUB), sk = uniform(kst * 16 * KSUB);
+  const int32_t qw = PK ? uniform(kst * wk) : qk;
+  // Byte steps between a lane's pieces: sub-step s and half h.  Row-major:
+  // consecutive bytes of the row; packed: 1 KB apart (one load instruction
+  // of the wavefront reads 1 KB of consecutive bytes).
+  constexpr uint32_t kS = PK ? 2048u : 32u, kH = PK ? 1024u : 16u;
 #pragma unroll
   for (int jb = 0; jb < NBW; ++jb) {
 #pragma unroll
     for (int s = 0; s < KSUB; ++s) {
-      st.w[jb][s][0] = __builtin_amdgcn_raw_buffer_load_b128(it.w, it.w_voff[jb] + 32u * s, qk, 0);
-      st.w[jb][s][1] = __builtin_amdgcn_raw_buffer_load_b128(it.w, it.w_voff[jb] + 32u * s + 16u, qk, 0);
+      st.w[jb][s][0] = __builtin_amdgcn_raw_buffer_load_b128(it.w, it.w_voff[jb] + kS * s, qw, 0);
+      st.w[jb][s][1] = __builtin_amdgcn_raw_buffer_load_b128(it.w, it.w_voff[jb] + kS * s + kH, qw, 0);
     }
     if constexpr (!SL) load_scales<KSUB>(st.ws[jb], it.ws, it.ws_voff[jb], sk);
   }
@@ -432,8 +446,14 @@ __device__ __forceinline__ void epilogue(float4_t (&acc)[NBW][MB], const ItemPos
   }
 }
 
-template <int MB, int NBW, int KSUB, int WAVES, bool SL>
-__global__ __launch_bounds__(WAVES * 64) void k_grouped_gemm(const GemmArgs p) {
+// One-row-block tiles with 256-element stages, or 512-element stages whose
+// weight scales come through LDS, fit two wavefronts per SIMD (at most 256
+// registers): ask for that so the allocator does not drift past it.
+template <int MB, int NBW, int KSUB, int WAVES, bool SL, bool PK>
+__global__ __launch_bounds__(WAVES * 64)
+__attribute__((amdgpu_waves_per_eu(MB == 1 && (KSUB == 1 || (KSUB == 2 && SL)) ? 2 : 1)))
+void k_grouped_gemm(const GemmArgs p) {
+  static_assert(!PK || NBW == 4, "packed weights are read by 64-column items");
   constexpr int BM = 16 * MB;
   constexpr int NTHR = WAVES * 64;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -504,7 +524,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_grouped_gemm(const GemmArgs p) {
   ItemLoads<MB, NBW> l0, l1;
   int32_t ld_round = 0, ld_st = 0, cp_round = 0, cp_st = 0;
   ld_pos = locate(item_of(0), 0, wl, p, 16 * MB, 16 * NBW, lane);
-  item_loads<MB, NBW, KSUB>(ld_pos, p, lane, l0);
+  item_loads<MB, NBW, KSUB, PK>(ld_pos, p, lane, l0);
   // nx: the item after ld's, located a stage or more before it is needed
   // (the last item repeats itself; that copy is never used).
   auto locate_next = [&](int32_t round) {
@@ -520,7 +540,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_grouped_gemm(const GemmArgs p) {
       ld_st = 0;
       ++ld_round;
       ld_pos = nx;
-      item_loads<MB, NBW, KSUB>(ld_pos, p, lane, dst);
+      item_loads<MB, NBW, KSUB, PK>(ld_pos, p, lane, dst);
       locate_next(ld_round);
     } else {
       dst = src;
@@ -564,11 +584,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_grouped_gemm(const GemmArgs p) {
   // around loads) but with out-of-range offsets, so it moves no data.
   Stage<MB, NBW, KSUB> s0, s1;
   uint32_t wsd[NBW][KSUB];
-  issue_loads<MB, NBW, KSUB, SL>(s0, l0, a_rs, as_rs, ld_st, line_copy(ld_round, ld_st), n, nbk);
+  issue_loads<MB, NBW, KSUB, SL, PK>(s0, l0, a_rs, as_rs, ld_st, line_copy(ld_round, ld_st), n, nbk);
   for (int32_t u = 0;; u += 2) {
     const bool more1 = u + 1 < units;
     if (more1) advance(l1, l0); else l1 = nowhere<MB, NBW>(l0);
-    issue_loads<MB, NBW, KSUB, SL>(s1, l1, a_rs, as_rs, ld_st,
+    issue_loads<MB, NBW, KSUB, SL, PK>(s1, l1, a_rs, as_rs, ld_st,
                                    more1 ? line_copy(ld_round, ld_st) : LineCopy{sl_base + 2 * kBufBytes, -1},
                                    n, nbk);
     // Without the uniform branches of SL kernels, keep the scheduler from
@@ -582,7 +602,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_grouped_gemm(const GemmArgs p) {
     if (!more1) break;
     const bool more2 = u + 2 < units;
     if (more2) advance(l0, l1); else l0 = nowhere<MB, NBW>(l1);
-    issue_loads<MB, NBW, KSUB, SL>(s0, l0, a_rs, as_rs, ld_st,
+    issue_loads<MB, NBW, KSUB, SL, PK>(s0, l0, a_rs, as_rs, ld_st,
                                    more2 ? line_copy(ld_round, ld_st) : LineCopy{sl_base + 2 * kBufBytes, -1},
                                    n, nbk);
     if constexpr (!SL) __builtin_amdgcn_sched_barrier(0);
@@ -627,9 +647,9 @@ hipError_t resident_groups_of(const void* kern, int threads, size_t lds, int* ou
 
 namespace {
 
-template <int MB, int NBW, int KSUB, int WAVES, bool SL>
+template <int MB, int NBW, int KSUB, int WAVES, bool SL, bool PK = false>
 hipError_t launch_tile(const GemmArgs& p, hipStream_t stream) {
-  auto kern = k_grouped_gemm<MB, NBW, KSUB, WAVES, SL>;
+  auto kern = k_grouped_gemm<MB, NBW, KSUB, WAVES, SL, PK>;
   const size_t lds = worklist_bytes(p.num_experts) + (SL ? (size_t)WAVES * scale_lds_per_wave<NBW>() : 0);
   int resident = 0;
   hipError_t err = resident_groups(kern, WAVES * 64, lds, &resident);
@@ -705,12 +725,12 @@ int64_t gemm_lds_bytes(const GemmTile& t, int32_t num_experts) {
   return b;
 }
 
-template <int NBW, int KSUB, bool SL>
+template <int NBW, int KSUB, bool SL, bool PK = false>
 hipError_t launch_mb(const GemmArgs& p, int m_blocks, hipStream_t stream) {
   switch (m_blocks) {
-    case 1: return launch_tile<1, NBW, KSUB, 4, SL>(p, stream);
-    case 2: return launch_tile<2, NBW, KSUB, 4, SL>(p, stream);
-    case 4: return launch_tile<4, NBW, KSUB, 4, SL>(p, stream);
+    case 1: return launch_tile<1, NBW, KSUB, 4, SL, PK>(p, stream);
+    case 2: return launch_tile<2, NBW, KSUB, 4, SL, PK>(p, stream);
+    case 4: return launch_tile<4, NBW, KSUB, 4, SL, PK>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -727,6 +747,12 @@ hipError_t launch_mb_k1024(const GemmArgs& p, int m_blocks, hipStream_t stream) 
 
 template <bool SL>
 hipError_t launch_sl(const GemmArgs& p, const GemmTile& t, hipStream_t stream) {
+  if (p.w_packed) {
+    // The packed layout's granule fixes the stage: k_sub = 2 iff k % 512 == 0.
+    if (t.n_blocks != 4 || t.k_sub != packed_granule(p.k) / kKStep) return hipErrorInvalidValue;
+    return t.k_sub == 2 ? launch_mb<4, 2, SL, true>(p, t.m_blocks, stream)
+                        : launch_mb<4, 1, SL, true>(p, t.m_blocks, stream);
+  }
   if (t.n_blocks == 4) {
     if (t.k_sub == 4) return hipErrorInvalidValue;
     return t.k_sub == 2 ? launch_mb<4, 2, SL>(p, t.m_blocks, stream)

@@ -94,6 +94,10 @@ __global__ __launch_bounds__(kThreads) void k_grouped_gemm_tiled(const GemmArgs 
   const rsrc_t a_rs = make_rsrc(p.a_q, (uint32_t)(p.a_rows * kb));
   const rsrc_t as_rs = make_rsrc(p.a_sf, (uint32_t)(p.a_rows * nbk));
   const int32_t a_last = (int32_t)p.a_rows - 1;
+  // Packed weight layout: bytes of a 16-row block, and log2 of the stages per
+  // granule (a granule of 256 or 512 elements holds 4 or 8 stages of 64).
+  const int32_t pk_block = packed_block_bytes(packed_granule(p.k));
+  const int32_t pk_lg = packed_granule(p.k) == 512 ? 3 : 2;
 
   int32_t from = 0;
   for (int32_t j = 0; j < my_items; ++j) {
@@ -106,11 +110,26 @@ __global__ __launch_bounds__(kThreads) void k_grouped_gemm_tiled(const GemmArgs 
     // n: out of range, reads zeros).
     rsrc_t rq, rs;
     uint32_t voff_q, voff_s;
+    uint32_t half = 16;  // bytes from a stage's first 16 code bytes to its second
+    int32_t wrg = 0;     // packed weights: 16-row blocks in this wave's 64-row group
     if (is_w) {
       rq = make_rsrc(p.w_q + (int64_t)it.e * n * kb, (uint32_t)(n * kb));
       rs = make_rsrc(p.w_sf + (int64_t)it.e * n * nbk, (uint32_t)(n * nbk));
       const int32_t row = it.n0 + lrow;
-      voff_q = row < n ? (uint32_t)(row * kb) : kOutOfRange;
+      if (p.w_packed) {
+        // This wave's 64 rows are one group of the packed layout; a thread's
+        // row is piece r of each 16-row block j of the group.
+        const int32_t grp0 = uniform(it.n0 + (lrow & ~(kPackRows - 1)));
+        // (A group wholly past n has no blocks: its rows read out of range and
+        // its stage offsets stay small and non-negative.)
+        const int32_t left = grp0 < n ? (n - grp0) / 16 : 0;
+        wrg = left < 4 ? left : 4;
+        const int32_t j = (row - grp0) >> 4, r = row & 15;
+        voff_q = row < n ? (uint32_t)(grp0 * kb + j * pk_block + 16 * r) : kOutOfRange;
+        half = 1024;
+      } else {
+        voff_q = row < n ? (uint32_t)(row * kb) : kOutOfRange;
+      }
       voff_s = row < n ? (uint32_t)(row * nbk) : kOutOfRange;
     } else {
       const int32_t r = it.row0 + (lrow < it.rows_valid ? lrow : 0);
@@ -134,12 +153,23 @@ __global__ __launch_bounds__(kThreads) void k_grouped_gemm_tiled(const GemmArgs 
     // of range (no traffic).
     u32x4_t q0[PD], q1[PD];
     uint32_t sc[PD];
+    // Byte offset of stage st's codes: row-major, 32 bytes per stage along the
+    // row; packed (weight waves), the stage's 32 bytes of a row are two
+    // 16-byte pieces 1 KB apart in block j of granule t, at the position of
+    // sub-step s and lane group g of the packed order.
+    const bool wpk = is_w && p.w_packed;
+    auto stage_off = [&](int32_t st) -> int32_t {
+      if (!wpk) return st * (kTK / 2);
+      const int32_t t = st >> pk_lg, m = st & ((1 << pk_lg) - 1);
+      const int32_t g = m >> (pk_lg - 2), sub = m & ((1 << (pk_lg - 2)) - 1);
+      return t * wrg * pk_block + sub * 2048 + g * 256;
+    };
     auto load_stage = [&](int slot, int32_t st) {
       const bool in = st < nst;
       const uint32_t oq = in ? voff_q : kOutOfRange, os = in ? voff_s : kOutOfRange;
-      const int32_t kq = uniform(st * (kTK / 2)), ks = uniform(st * (kTK / 16));
+      const int32_t kq = uniform(stage_off(st)), ks = uniform(st * (kTK / 16));
       q0[slot] = __builtin_amdgcn_raw_buffer_load_b128(rq, oq, kq, 0);
-      q1[slot] = __builtin_amdgcn_raw_buffer_load_b128(rq, oq + 16u, kq, 0);
+      q1[slot] = __builtin_amdgcn_raw_buffer_load_b128(rq, oq + half, kq, 0);
       sc[slot] = __builtin_amdgcn_raw_buffer_load_b32(rs, os, ks, 0);
     };
     // Issue the ring in slot order (kept by the scheduling barriers) so the

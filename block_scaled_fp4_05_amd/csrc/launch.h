@@ -27,6 +27,16 @@ struct GemmTile {
 
 constexpr int kKStep = 256;  // K granularity the kernels require
 
+// Packed weight layout (moe_fp4_pack_weights): K elements per granule, and the
+// bytes of one 16-row x granule block.  Rows are grouped by 64.
+__host__ __device__ constexpr int32_t packed_granule(int64_t k) { return k % 512 == 0 ? 512 : 256; }
+__host__ __device__ constexpr int32_t packed_block_bytes(int32_t granule) { return 8 * granule; }
+constexpr int kPackRows = 64;
+
+// Rearrange weight codes between the row-major and the packed layout.
+hipError_t launch_repack(const uint8_t* src, uint8_t* dst, int32_t num_experts, int64_t n,
+                         int64_t k, bool to_packed, hipStream_t stream);
+
 // The tile used for a problem with these sizes; `env` (may be NULL) is the
 // value of MOE_FP4_TILE ("MxN" or "MxNxK": M rows per item, N columns per
 // wave, K elements per pipeline stage; a trailing 'r' keeps the weight block
@@ -52,7 +62,8 @@ struct GemmArgs {
   int64_t k;
   int64_t ldo;
   int32_t num_experts;
-  int32_t n_tiles;  // ceil(n / (16 * n_blocks))
+  int32_t n_tiles;   // ceil(n / (16 * n_blocks))
+  int32_t w_packed;  // w_q is in the packed layout
 };
 
 hipError_t launch_grouped_gemm(const GemmArgs& args, const GemmTile& tile, hipStream_t stream);

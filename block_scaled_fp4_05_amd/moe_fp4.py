@@ -19,7 +19,8 @@ IN_BF16, IN_FP32 = 0, 1
 SCALE_STATIC, SCALE_DYNAMIC = 0, 1
 
 # Every symbol include/moe_fp4.h declares.
-EXPORTED = ("moe_fp4_quantize", "moe_grouped_gemm_fp4", "moe_grouped_gemm_fp4_plan",
+EXPORTED = ("moe_fp4_quantize", "moe_grouped_gemm_fp4", "moe_grouped_gemm_fp4_packed",
+            "moe_fp4_pack_weights", "moe_fp4_unpack_weights", "moe_grouped_gemm_fp4_plan",
             "moe_fp4_stage_bytes", "moe_fp4_status_string", "moe_fp4_abi_version")
 
 
@@ -52,6 +53,11 @@ def lib() -> ctypes.CDLL:
     L.moe_grouped_gemm_fp4.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp, vp, i32, i64, i64, i64,
                                        vp, i64, vp]
     L.moe_grouped_gemm_fp4.restype = i
+    L.moe_grouped_gemm_fp4_packed.argtypes = L.moe_grouped_gemm_fp4.argtypes
+    L.moe_grouped_gemm_fp4_packed.restype = i
+    for f in (L.moe_fp4_pack_weights, L.moe_fp4_unpack_weights):
+        f.argtypes = [vp, vp, i32, i64, i64, vp]
+        f.restype = i
     L.moe_grouped_gemm_fp4_plan.argtypes = [i32, i64, i64, i64, ctypes.POINTER(Plan)]
     L.moe_grouped_gemm_fp4_plan.restype = i
     L.moe_fp4_stage_bytes.argtypes = [i64, i64, i64]
@@ -105,6 +111,34 @@ def gemm_raw(*args):
     return lib().moe_grouped_gemm_fp4(*args)
 
 
+def gemm_packed_raw(*args):
+    """moe_grouped_gemm_fp4_packed with raw pointers; returns the status code."""
+    return lib().moe_grouped_gemm_fp4_packed(*args)
+
+
+def pack_weights(w_q: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Row-major weight codes [E][n][k/2] (uint8, CUDA) -> the packed layout the
+    packed GEMM reads (same shape and size; a byte permutation)."""
+    E, n, kb = w_q.shape
+    if out is None:
+        out = torch.empty_like(w_q)
+    st = lib().moe_fp4_pack_weights(_ptr(w_q), _ptr(out), E, n, 2 * kb, _stream(stream))
+    if st != OK:
+        raise MoeFp4Error(st, "moe_fp4_pack_weights")
+    return out
+
+
+def unpack_weights(w_packed: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Inverse of pack_weights."""
+    E, n, kb = w_packed.shape
+    if out is None:
+        out = torch.empty_like(w_packed)
+    st = lib().moe_fp4_unpack_weights(_ptr(w_packed), _ptr(out), E, n, 2 * kb, _stream(stream))
+    if st != OK:
+        raise MoeFp4Error(st, "moe_fp4_unpack_weights")
+    return out
+
+
 def quantize(x: torch.Tensor, tensor_scale: torch.Tensor | None = None, q=None, sf=None,
              stream=None, dynamic: bool | None = None):
     """NVFP4-quantise a 2-D BF16 or FP32 CUDA tensor [rows][k].
@@ -143,11 +177,12 @@ def quantize(x: torch.Tensor, tensor_scale: torch.Tensor | None = None, q=None, 
 
 
 def grouped_gemm(a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets, a_row_index=None, out=None,
-                 m_total: int | None = None, stream=None):
+                 m_total: int | None = None, stream=None, packed: bool = False):
     """NVFP4 grouped GEMM.  Shapes: a_q [a_rows][k/2], a_sf [a_rows][k/16], a_scale [1],
     w_q [E][n][k/2], w_sf [E][n][k/16], w_scale [E], offsets int32 [E+1],
     a_row_index int32 [m_total] or None.  m_total defaults to a_row_index's length,
-    else a_rows.  Returns out, a BF16 tensor [m_total][n] (or the given `out`)."""
+    else a_rows.  packed: w_q is in the packed layout (pack_weights).  Returns out,
+    a BF16 tensor [m_total][n] (or the given `out`)."""
     E, n, kb = w_q.shape
     k = 2 * kb
     a_rows = a_q.shape[0]
@@ -155,9 +190,9 @@ def grouped_gemm(a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets, a_row_index=No
         m_total = a_row_index.shape[0] if a_row_index is not None else a_rows
     if out is None:
         out = torch.empty((m_total, n), dtype=torch.bfloat16, device=w_q.device)
-    st = lib().moe_grouped_gemm_fp4(
-        _ptr(a_q), _ptr(a_sf), _ptr(a_scale), a_rows, _ptr(a_row_index), _ptr(w_q), _ptr(w_sf),
-        _ptr(w_scale), _ptr(offsets), E, m_total, n, k, _ptr(out), out.stride(0), _stream(stream))
+    fn = lib().moe_grouped_gemm_fp4_packed if packed else lib().moe_grouped_gemm_fp4
+    st = fn(_ptr(a_q), _ptr(a_sf), _ptr(a_scale), a_rows, _ptr(a_row_index), _ptr(w_q), _ptr(w_sf),
+            _ptr(w_scale), _ptr(offsets), E, m_total, n, k, _ptr(out), out.stride(0), _stream(stream))
     if st != OK:
-        raise MoeFp4Error(st, "moe_grouped_gemm_fp4")
+        raise MoeFp4Error(st, "moe_grouped_gemm_fp4_packed" if packed else "moe_grouped_gemm_fp4")
     return out

@@ -52,7 +52,8 @@ enum {
   MOE_FP4_ERR_ALIGN = 3,       /* a pointer or leading dimension is misaligned       */
   MOE_FP4_ERR_UNSUPPORTED = 4, /* well-formed but outside what the kernels handle    */
   MOE_FP4_ERR_HIP = 5,         /* the HIP runtime reported an error                  */
-  MOE_FP4_ERR_ARG = 6          /* an enumerated argument has an unknown value        */
+  MOE_FP4_ERR_ARG = 6          /* an enumerated argument has an unknown value, or    */
+                               /* buffers that must be distinct overlap              */
 };
 
 /* Input element types of moe_fp4_quantize. */
@@ -154,6 +155,55 @@ int moe_grouped_gemm_fp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a
                          const int32_t* expert_offsets, int32_t num_experts,
                          int64_t m_total, int64_t n, int64_t k,
                          uint16_t* out, int64_t ldo, void* stream);
+
+/*
+ * Packed weight-code layout (MOE_FP4 "packed"), the layout
+ * moe_grouped_gemm_fp4_packed reads.  Expert weights are constant across
+ * calls, so they can be rearranged once, off the critical path, into the order
+ * the GEMM's wavefronts load them: every load instruction then reads one
+ * contiguous 1 KB and every pipeline stage one contiguous block, instead of 64
+ * row segments a row pitch apart.  It permutes the bytes of w_q only (w_sf
+ * keeps the row-major layout above) and keeps each expert's size and position:
+ *   G  = 512 if k % 512 == 0, else 256   (K elements per granule)
+ *   GB = G / 2                           (code bytes of one row per granule)
+ *   Rows are taken in groups of 64 (the last group of an expert may hold
+ *   16*rg rows, rg = 1..3).  Group q occupies the bytes that rows 64q .. of
+ *   the row-major layout occupy, starting at 64*q*(k/2).
+ *   Inside group q, granule t, row block j (rows 64q + 16j .. +15) is a block
+ *   of 8*G bytes at offset (t*rg + j) * 8*G (rg = 4 for a full group).
+ *   Inside a block, the 16-byte piece at offset 16*(((2*s + h)*4 + g)*16 + r)
+ *   (s < G/256, h < 2, g < 4, r < 16) holds row 64q + 16j + r, row-major code
+ *   bytes t*GB + (GB/4)*g + 32*s + 16*h .. +15.
+ */
+
+/*
+ * moe_fp4_pack_weights -- rearrange row-major weight codes w_q
+ * [num_experts][n][k/2] into the packed layout above (w_packed, same size).
+ * moe_fp4_unpack_weights is the inverse.  A pure byte permutation.
+ *   src, dst     device, num_experts * n * k/2 bytes each, 16-byte aligned, not
+ *                overlapping.
+ *   n            >= 1, a multiple of 16; k >= 1, a multiple of 256.
+ * Errors: NULL, SHAPE (num_experts < 1, n < 1, k < 1), ALIGN, UNSUPPORTED
+ * (n % 16, k % 256, n * k/2 >= 2^31 - 4096), ARG (src and dst overlap), HIP.
+ */
+int moe_fp4_pack_weights(const uint8_t* w_q, uint8_t* w_packed, int32_t num_experts,
+                         int64_t n, int64_t k, void* stream);
+int moe_fp4_unpack_weights(const uint8_t* w_packed, uint8_t* w_q, int32_t num_experts,
+                           int64_t n, int64_t k, void* stream);
+
+/*
+ * moe_grouped_gemm_fp4_packed -- moe_grouped_gemm_fp4 with w_q in the packed
+ * layout (written by moe_fp4_pack_weights).  Same arguments, result bits,
+ * preconditions and errors; in addition UNSUPPORTED when MOE_FP4_TILE asks
+ * for a K step other than the granule G or a width other than 64 columns per
+ * wavefront.
+ */
+int moe_grouped_gemm_fp4_packed(const uint8_t* a_q, const uint8_t* a_sf, const float* a_scale,
+                                int64_t a_rows, const int32_t* a_row_index,
+                                const uint8_t* w_packed, const uint8_t* w_sf,
+                                const float* w_scale, const int32_t* expert_offsets,
+                                int32_t num_experts, int64_t m_total, int64_t n, int64_t k,
+                                uint16_t* out, int64_t ldo, void* stream);
 
 /* Kernel configuration the GEMM picks for a problem (host-only, no GPU call). */
 typedef struct {

@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from conftest import ROOT, read_golden
@@ -131,3 +132,64 @@ def test_gemm_rejects(kw, status):
 @needs_no_gpu
 def test_gemm_empty_problem_is_a_noop():
     assert _g(m=0, a_rows=0) == 0
+
+
+def _gp(**kw):
+    a = dict(a_q=P16, a_sf=P16, a_scale=P16, a_rows=64, idx=None, w_q=P16, w_sf=P16, w_scale=P16,
+             off=P16, E=4, m=64, n=64, k=512, out=P16, ldo=64, stream=None)
+    a.update(kw)
+    return _lib().gemm_packed_raw(a["a_q"], a["a_sf"], a["a_scale"], a["a_rows"], a["idx"], a["w_q"],
+                                  a["w_sf"], a["w_scale"], a["off"], a["E"], a["m"], a["n"], a["k"],
+                                  a["out"], a["ldo"], a["stream"])
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("kw,status", [
+    (dict(w_q=None), 1), (dict(out=None), 1), (dict(E=0), 2), (dict(n=0), 2), (dict(ldo=32), 2),
+    (dict(n=24, ldo=24), 4), (dict(k=320), 4), (dict(w_q=P16 + 8), 3),
+])
+def test_packed_gemm_rejects(kw, status):
+    assert _gp(**kw) == status
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("tile", ["16x32", "16x64x256", "32x32x512"])
+def test_packed_gemm_rejects_tiles_the_layout_cannot_feed(tile, monkeypatch):
+    # k = 512: the packed granule is 512 elements and items are 64 columns wide.
+    monkeypatch.setenv("MOE_FP4_TILE", tile)
+    assert _gp() == 4
+
+
+def _rp(fn, **kw):
+    a = dict(src=P16, dst=P16 * 64, E=2, n=64, k=512, stream=None)
+    a.update(kw)
+    return getattr(_lib().lib(), fn)(a["src"], a["dst"], a["E"], a["n"], a["k"], a["stream"])
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("fn", ["moe_fp4_pack_weights", "moe_fp4_unpack_weights"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(src=None), 1), (dict(dst=None), 1), (dict(E=0), 2), (dict(n=0), 2), (dict(k=0), 2),
+    (dict(n=24), 4), (dict(k=320), 4), (dict(src=P16 + 8), 3), (dict(dst=P16 * 64 + 4), 3),
+    (dict(dst=P16 + 16), 6),
+])
+def test_repack_rejects(fn, kw, status):
+    assert _rp(fn, **kw) == status
+
+
+@pytest.mark.parametrize("n,k", [(16, 256), (48, 256), (64, 512), (80, 768), (144, 1024),
+                                 (112, 2048), (64, 6144)])
+def test_packed_layout_definition_is_a_group_preserving_permutation(n, k):
+    import pack_layout
+    kb = k // 2
+    src = pack_layout.source_offsets(n, k)
+    assert src.size * 16 == n * kb
+    assert np.array_equal(np.sort(src), np.arange(0, n * kb, 16))
+    # Every 64-row group keeps its byte range: packed offset and source share the group.
+    dst = np.arange(src.size) * 16
+    assert np.array_equal(dst // (64 * kb), src // (64 * kb))
+    # One packed 1 KB run is one load instruction: 16 rows x 4 lane groups, same K piece.
+    G = 512 if k % 512 == 0 else 256
+    first = src[:64]
+    assert np.array_equal(first[:16] // kb, np.arange(16))
+    assert np.array_equal(first[16:32] - first[:16], np.full(16, G // 8))

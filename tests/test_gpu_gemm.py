@@ -39,7 +39,9 @@ def _random_problem(E, rows, n, k, seed, a_rows=None, scale_lo=0x20, scale_hi=0x
         offsets=off, m_total=m)
 
 
-def _gpu_gemm(P, a_row_index=None, ldo=None, extra_rows=0, tile=None):
+def _gpu_gemm(P, a_row_index=None, ldo=None, extra_rows=0, tile=None, packed=False):
+    """Run the GEMM; packed=True packs the weight codes on the GPU first and calls
+    the packed entry point."""
     from block_scaled_fp4_05_amd import moe_fp4
     n = P["w_q"].shape[1]
     m = P["m_total"]
@@ -50,11 +52,14 @@ def _gpu_gemm(P, a_row_index=None, ldo=None, extra_rows=0, tile=None):
     if tile:
         os.environ["MOE_FP4_TILE"] = tile
     try:
+        w_q = dev(P["w_q"])
+        if packed:
+            w_q = moe_fp4.pack_weights(w_q)
         moe_fp4.grouped_gemm(
             dev(P["a_q"]), dev(P["a_sf"]), dev(np.array([P["a_scale"]], np.float32)),
-            dev(P["w_q"]), dev(P["w_sf"]), dev(P["w_scale"]), dev(P["offsets"]),
+            w_q, dev(P["w_sf"]), dev(P["w_scale"]), dev(P["offsets"]),
             a_row_index=None if a_row_index is None else dev(a_row_index.astype(np.int32)),
-            out=out_full, m_total=m)
+            out=out_full, m_total=m, packed=packed)
     finally:
         if tile:
             if old is None:
@@ -203,3 +208,58 @@ def test_quantise_then_gemm_chain_c3():
     got = bf16_bits_of(out)
     sel = wl_data.sample_rows(P["offsets"], 48, 32)
     _check_rows(got, P, rows_sel=sel, a_row_index=idx, label="chain")
+
+
+# ------------------------------------------------------ packed weights --
+
+@pytest.mark.parametrize("E,n,k", [(2, 64, 256), (3, 80, 768), (2, 128, 1024), (1, 48, 2048),
+                                   (2, 208, 6144)])
+def test_pack_matches_the_layout_definition_and_unpack_inverts_it(E, n, k):
+    import pack_layout
+    from block_scaled_fp4_05_amd import moe_fp4
+    w = gen.random_fp4_bytes((E, n, k // 2), 900 + n)
+    say(f"pack E={E} n={n} k={k}")
+    pk = moe_fp4.pack_weights(dev(w))
+    back = moe_fp4.unpack_weights(pk)
+    torch.cuda.synchronize()
+    assert np.array_equal(pk.cpu().numpy(), pack_layout.pack(w))
+    assert np.array_equal(back.cpu().numpy(), w)
+
+
+# (E, rows per expert, n, k): m-blocks 1/2/4 and the workgroup tile, K steps of
+# 256 and 512 elements, scales through registers and through LDS, and a last
+# 64-row group holding 16, 32 or 48 rows.
+PACKED_CASES = [
+    (3, [5, 16, 9], 64, 256),
+    (4, [16, 0, 7, 12], 80, 512),
+    (2, [20, 31], 112, 1024),
+    (3, [40, 64, 33], 144, 768),
+    (2, [9, 16], 208, 2048),
+    (2, [12, 3], 64, 6144),
+    (2, [130, 100], 176, 512),
+    (1, [150], 96, 2048),
+    (2, [100, 120], 80, 768),
+]
+
+
+@pytest.mark.parametrize("case", range(len(PACKED_CASES)))
+def test_packed_gemm_bit_equals_rowmajor_and_meets_the_oracle(case):
+    E, rows, n, k = PACKED_CASES[case]
+    P = _random_problem(E, rows, n, k, 700 + case, a_rows=sum(rows) + 3)
+    idx = np.random.default_rng(701 + case).integers(0, sum(rows) + 3, P["m_total"]).astype(np.int32)
+    say(f"packed gemm E={E} rows={rows} n={n} k={k}")
+    ref = _gpu_gemm(P, a_row_index=idx, extra_rows=2)
+    got = _gpu_gemm(P, a_row_index=idx, extra_rows=2, packed=True)
+    assert np.array_equal(got, ref)
+    _check_rows(got, P, a_row_index=idx, label=f"packed case {case}")
+
+
+@pytest.mark.parametrize("name,count", [("c3", 64), ("c4", 32), ("c5", 32)])
+def test_packed_full_size_workload(name, count):
+    P, idx = _workload_problem(name)
+    say(f"packed gemm workload {name}")
+    ref = _gpu_gemm(P, a_row_index=idx)
+    got = _gpu_gemm(P, a_row_index=idx, packed=True)
+    assert np.array_equal(got, ref)
+    sel = wl_data.sample_rows(P["offsets"], count, 33)
+    _check_rows(got, P, rows_sel=sel, a_row_index=idx, label=f"packed {name}")
