@@ -27,7 +27,8 @@ int check_gemm_shape(int32_t num_experts, int64_t m_total, int64_t n, int64_t k)
   if (num_experts < 1 || m_total < 0 || n < 1 || k < 1) return MOE_FP4_ERR_SHAPE;
   if (num_experts > kMaxExperts) return MOE_FP4_ERR_UNSUPPORTED;
   if (n % 16 != 0 || k % moe_fp4::kKStep != 0) return MOE_FP4_ERR_UNSUPPORTED;
-  if (n > INT32_MAX / 2 || m_total > INT32_MAX) return MOE_FP4_ERR_UNSUPPORTED;
+  // Row-index entries are addressed with 32-bit byte offsets.
+  if (n > INT32_MAX / 2 || m_total > INT32_MAX / 4 - 1024) return MOE_FP4_ERR_UNSUPPORTED;
   // One expert's packed weights are addressed with 32-bit buffer offsets.
   if (n * (k / 2) > (int64_t)INT32_MAX - 4096) return MOE_FP4_ERR_UNSUPPORTED;
   // The work-list counts items in int32: bound the largest possible count.

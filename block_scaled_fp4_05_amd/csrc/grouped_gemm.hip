@@ -58,19 +58,6 @@ constexpr int kSpan = 2048;
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
-// v_writelane_b32: lane J of `v` takes the wavefront-uniform value `s`.
-template <int J>
-__device__ __forceinline__ int32_t write_lane(int32_t v, int32_t s) {
-  asm("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(s), "n"(J));
-  return v;
-}
-
-template <int J>
-__device__ __forceinline__ int32_t gather16(int32_t v, const int32_t (&s)[16]) {
-  if constexpr (J < 16) return gather16<J + 1>(write_lane<J>(v, s[J]), s);
-  else return v;
-}
-
 // LDS bytes per wave for staged weight scales: two span buffers of 16*NBW
 // rows x 128 bytes, and a 1 KB sink for the copies issued by stages that start
 // no span (see issue_loads).
@@ -133,13 +120,33 @@ __device__ __forceinline__ ItemLoads<MB, NBW> nowhere(const ItemLoads<MB, NBW>& 
   return z;
 }
 
+// Lane (c, g)'s entry of the row index for row block ib of an item: a vector
+// load issued an item ahead of its use (so its latency is hidden behind a
+// unit of work, where scalar loads would stall the wave when it is needed).
+// Rows past the expert's end repeat its first row: their products are
+// computed and never stored.  Without a row index the resource is empty, the
+// load returns nothing and the caller takes the row itself.
+__device__ __forceinline__ uint32_t row_index_load(const rsrc_t& idx_rs, const ItemPos& it, int ib,
+                                                   int c) {
+  const int32_t rr = 16 * ib + c;
+  const int32_t r = it.row0 + (rr < it.rows_valid ? rr : 0);
+  return __builtin_amdgcn_raw_buffer_load_b32(idx_rs, (uint32_t)(4 * r), 0, 0);
+}
+
 // The per-lane loads of a located item: this expert's weight resources and
-// each lane's byte offsets.  The 16 row numbers of a row block are read as
-// scalars through the row index, written into lanes 0..15 and spread to every
-// 16-lane group.
+// each lane's byte offsets.  `rows[ib]` is the lane's row-index entry for row
+// block ib (row_index_load).
+// Row x pitch for lane offsets.  The host bounds rows * (k/2) below 2^31 with
+// k/2 >= 128, so both factors are below 2^24 and the 24-bit multiply is exact;
+// it also keeps the compiler from a 64-bit multiply-add whose unused high half
+// would wait on loads still in flight in that register.
+__device__ __forceinline__ uint32_t mul24(int32_t a, int32_t b) {
+  return __umul24((uint32_t)a, (uint32_t)b);
+}
+
 template <int MB, int NBW, int KSUB, bool PK>
 __device__ __forceinline__ void item_loads(const ItemPos& it, const GemmArgs& p, int lane,
-                                           ItemLoads<MB, NBW>& ld) {
+                                           const uint32_t (&rows)[MB], ItemLoads<MB, NBW>& ld) {
   const int c = lane & 15, g = lane >> 4;
   // 32-bit offsets: the host guarantees n * k/2 and a_rows * k/2 < 2^31.
   const int32_t n = (int32_t)p.n, kb = (int32_t)(p.k >> 1), nbk = (int32_t)(p.k >> 4);
@@ -153,35 +160,26 @@ __device__ __forceinline__ void item_loads(const ItemPos& it, const GemmArgs& p,
   for (int jb = 0; jb < NBW; ++jb) {
     const int32_t row = it.n0 + 16 * jb + c;
     const bool ok = row < n;
-    const int32_t wv = PK ? it.n0 * kb + jb * kBlock + 16 * lane : row * kb + 32 * KSUB * g;
-    ld.w_voff[jb] = ok ? (uint32_t)wv : kOutOfRange;
-    ld.ws_voff[jb] = ok ? (uint32_t)(row * nbk + 4 * KSUB * g) : kOutOfRange;
+    const uint32_t wv = PK ? (uint32_t)(it.n0 * kb + jb * kBlock + 16 * lane)
+                           : mul24(row, kb) + 32 * KSUB * g;
+    ld.w_voff[jb] = ok ? wv : kOutOfRange;
+    ld.ws_voff[jb] = ok ? mul24(row, nbk) + 4 * KSUB * g : kOutOfRange;
   }
   // Scale-line copies move 8 rows x 128 bytes per instruction: lane l takes
   // row l/8 and stores the row's 16-byte chunk (l%8) ^ (row%8) in LDS slot l%8,
   // a swizzle that spreads the later per-stage reads over the LDS banks.
   {
     const int r8 = lane >> 3, slot = lane & 7;
-    ld.sl_voff = (uint32_t)((it.n0 + r8) * nbk + 16 * (slot ^ r8));
+    ld.sl_voff = mul24(it.n0 + r8, nbk) + 16 * (slot ^ r8);
   }
-  const sconst_i32 idx = (sconst_i32)p.a_row_index;
   const int32_t a_last = (int32_t)p.a_rows - 1;
 #pragma unroll
   for (int ib = 0; ib < MB; ++ib) {
-    int32_t src[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      // Rows past the expert's end repeat its first row: their products are
-      // computed and never stored.
-      const int32_t rr = 16 * ib + j;
-      const int32_t r = it.row0 + (rr < it.rows_valid ? rr : 0);
-      src[j] = uniform(idx ? idx[r] : r);
-    }
-    int32_t mine = gather16<0>(0, src);
-    mine = __builtin_amdgcn_ds_bpermute(c << 2, mine);
+    const int32_t rr = 16 * ib + c;
+    int32_t mine = p.a_row_index ? (int32_t)rows[ib] : it.row0 + (rr < it.rows_valid ? rr : 0);
     mine = mine < 0 ? 0 : (mine > a_last ? a_last : mine);
-    ld.a_voff[ib] = (uint32_t)(mine * kb + 32 * KSUB * g);
-    ld.as_voff[ib] = (uint32_t)(mine * nbk + 4 * KSUB * g);
+    ld.a_voff[ib] = mul24(mine, kb) + 32 * KSUB * g;
+    ld.as_voff[ib] = mul24(mine, nbk) + 4 * KSUB * g;
   }
 }
 
@@ -449,10 +447,11 @@ __device__ __forceinline__ void epilogue(float4_t (&acc)[NBW][MB], const ItemPos
 // One-row-block tiles with 256-element stages, or 512-element stages whose
 // weight scales come through LDS, fit two wavefronts per SIMD (at most 256
 // registers): ask for that so the allocator does not drift past it.
-template <int MB, int NBW, int KSUB, int WAVES, bool SL, bool PK>
+template <int MB, int NBW, int KSUB, int WAVES, bool SL, bool PK, int R>
 __global__ __launch_bounds__(WAVES * 64)
 __attribute__((amdgpu_waves_per_eu(MB == 1 && (KSUB == 1 || (KSUB == 2 && SL)) ? 2 : 1)))
 void k_grouped_gemm(const GemmArgs p) {
+  static_assert(R == 2 || (R == 3 && !SL), "a third register stage only without scale lines");
   static_assert(!PK || NBW == 4, "packed weights are read by 64-column items");
   constexpr int BM = 16 * MB;
   constexpr int NTHR = WAVES * 64;
@@ -516,15 +515,22 @@ void k_grouped_gemm(const GemmArgs p) {
 #pragma unroll
     for (int ib = 0; ib < MB; ++ib) acc[jb][ib] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // ld_*: the unit whose loads are issued next; cp: the item being accumulated.
-  // Each register stage has its own set of lane offsets (l0 for s0, l1 for s1).
+  // A ring of R register stages.  Unit v (stage ld_st of the wave's item
+  // round ld_round) goes to slot v % R with its own lane offsets l[slot] and
+  // item position pos[slot]; the loads run R-1 units ahead of the unit being
+  // computed.  cp_round / cp_st count the unit being computed.
   // nx: the item after ld's, located and with its scalar loads in flight.
   const WorkList wl{prefix, offl};
-  ItemPos ld_pos, cp, nx;
-  ItemLoads<MB, NBW> l0, l1;
+  ItemPos ld_pos, nx, pos[R];
+  ItemLoads<MB, NBW> l[R];
   int32_t ld_round = 0, ld_st = 0, cp_round = 0, cp_st = 0;
+  // Row-index entries: of the item being started (first item), then of nx.
+  const rsrc_t idx_rs = make_rsrc(p.a_row_index, p.a_row_index ? (uint32_t)(4 * m_total) : 0u);
+  uint32_t nrow[MB];
   ld_pos = locate(item_of(0), 0, wl, p, 16 * MB, 16 * NBW, lane);
-  item_loads<MB, NBW, KSUB, PK>(ld_pos, p, lane, l0);
+#pragma unroll
+  for (int ib = 0; ib < MB; ++ib) nrow[ib] = row_index_load(idx_rs, ld_pos, ib, c);
+  item_loads<MB, NBW, KSUB, PK>(ld_pos, p, lane, nrow, l[0]);
   // nx: the item after ld's, located a stage or more before it is needed
   // (the last item repeats itself; that copy is never used).
   auto locate_next = [&](int32_t round) {
@@ -532,7 +538,15 @@ void k_grouped_gemm(const GemmArgs p) {
     nx = locate(item_of(r), ld_pos.e, wl, p, 16 * MB, 16 * NBW, lane);
   };
   locate_next(0);
-  cp = ld_pos;
+  pos[0] = ld_pos;
+  // Fetch nx's row-index entries now; every later issue refetches them for
+  // the current nx, unconditionally (no load behind a branch), so they are a
+  // unit or more old when an item change consumes them.
+  auto prefetch_rows = [&]() {
+#pragma unroll
+    for (int ib = 0; ib < MB; ++ib) nrow[ib] = row_index_load(idx_rs, nx, ib, c);
+  };
+  prefetch_rows();
   // Move the load position to the next unit: a new item (already located)
   // gets its lane offsets in dst, otherwise dst takes src's offsets.
   auto advance = [&](ItemLoads<MB, NBW>& dst, const ItemLoads<MB, NBW>& src) {
@@ -540,7 +554,7 @@ void k_grouped_gemm(const GemmArgs p) {
       ld_st = 0;
       ++ld_round;
       ld_pos = nx;
-      item_loads<MB, NBW, KSUB, PK>(ld_pos, p, lane, dst);
+      item_loads<MB, NBW, KSUB, PK>(ld_pos, p, lane, nrow, dst);
       locate_next(ld_round);
     } else {
       dst = src;
@@ -553,12 +567,11 @@ void k_grouped_gemm(const GemmArgs p) {
 #pragma unroll
     for (int jb = 0; jb < NBW; ++jb) ps.data[jb][ib] = u32x2_t{0u, 0u};
   }
-  auto retire = [&]() {
+  auto retire = [&](const ItemPos& it) {
     if (++cp_st == nst) {
-      epilogue<MB, NBW>(acc, cp, c, g, p, ps);
+      epilogue<MB, NBW>(acc, it, c, g, p, ps);
       cp_st = 0;
       ++cp_round;
-      cp = ld_pos;
     }
   };
   // Weight scales of the stage about to be computed.
@@ -577,41 +590,43 @@ void k_grouped_gemm(const GemmArgs p) {
         for (int s = 0; s < KSUB; ++s) wsd[jb][s] = st.ws[jb][s];
     }
   };
+  // Issue unit v's loads into slot `to` (lane offsets advanced from slot
+  // `from`).  Past the last unit the issue still happens, keeping the code
+  // free of branches around loads, but with out-of-range offsets: no data.
+  Stage<MB, NBW, KSUB> s[R];
+  auto issue = [&](int to, int from, int32_t v) {
+    const bool more = v < units;
+    if (more) advance(l[to], l[from]); else l[to] = nowhere<MB, NBW>(l[from]);
+    pos[to] = ld_pos;
+    prefetch_rows();
+    issue_loads<MB, NBW, KSUB, SL, PK>(s[to], l[to], a_rs, as_rs, ld_st,
+                                       more ? line_copy(ld_round, ld_st)
+                                            : LineCopy{sl_base + 2 * kBufBytes, -1},
+                                       n, nbk);
+  };
 
-  // Two register stages.  Every iteration issues the next stage's loads before
-  // computing the current one, so one stage is always in flight; after the
-  // last unit the issue still happens (keeping the code free of branches
-  // around loads) but with out-of-range offsets, so it moves no data.
-  Stage<MB, NBW, KSUB> s0, s1;
   uint32_t wsd[NBW][KSUB];
-  issue_loads<MB, NBW, KSUB, SL, PK>(s0, l0, a_rs, as_rs, ld_st, line_copy(ld_round, ld_st), n, nbk);
-  for (int32_t u = 0;; u += 2) {
-    const bool more1 = u + 1 < units;
-    if (more1) advance(l1, l0); else l1 = nowhere<MB, NBW>(l0);
-    issue_loads<MB, NBW, KSUB, SL, PK>(s1, l1, a_rs, as_rs, ld_st,
-                                   more1 ? line_copy(ld_round, ld_st) : LineCopy{sl_base + 2 * kBufBytes, -1},
-                                   n, nbk);
-    // Without the uniform branches of SL kernels, keep the scheduler from
-    // sinking the next stage's loads into (or below) this stage's computation.
-    if constexpr (!SL) __builtin_amdgcn_sched_barrier(0);
-    stage_scales(s0, wsd);
-    compute_stage<MB, NBW, KSUB, SL>(s0, wsd, cp.rows_valid, acc);
-    hold<MB, NBW>(l0);
-    if constexpr (!SL) hold_stores<MB, NBW>(ps);
-    retire();
-    if (!more1) break;
-    const bool more2 = u + 2 < units;
-    if (more2) advance(l0, l1); else l0 = nowhere<MB, NBW>(l1);
-    issue_loads<MB, NBW, KSUB, SL, PK>(s0, l0, a_rs, as_rs, ld_st,
-                                   more2 ? line_copy(ld_round, ld_st) : LineCopy{sl_base + 2 * kBufBytes, -1},
-                                   n, nbk);
-    if constexpr (!SL) __builtin_amdgcn_sched_barrier(0);
-    stage_scales(s1, wsd);
-    compute_stage<MB, NBW, KSUB, SL>(s1, wsd, cp.rows_valid, acc);
-    hold<MB, NBW>(l1);
-    if constexpr (!SL) hold_stores<MB, NBW>(ps);
-    retire();
-    if (!more2) break;
+  issue_loads<MB, NBW, KSUB, SL, PK>(s[0], l[0], a_rs, as_rs, ld_st, line_copy(ld_round, ld_st), n, nbk);
+#pragma unroll
+  for (int r = 1; r < R - 1; ++r) issue(r, r - 1, r);
+  bool done = false;
+  for (int32_t u = 0; !done; u += R) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (done) break;
+      // Every step issues the unit R-1 ahead before computing this one, so
+      // R-1 units are always in flight.
+      issue((r + R - 1) % R, (r + R - 2) % R, u + r + R - 1);
+      // Without the uniform branches of SL kernels, keep the scheduler from
+      // sinking the next stage's loads into (or below) this stage's computation.
+      if constexpr (!SL) __builtin_amdgcn_sched_barrier(0);
+      stage_scales(s[r], wsd);
+      compute_stage<MB, NBW, KSUB, SL>(s[r], wsd, pos[r].rows_valid, acc);
+      hold<MB, NBW>(l[r]);
+      if constexpr (!SL) hold_stores<MB, NBW>(ps);
+      retire(pos[r]);
+      done = u + r + 1 >= units;
+    }
   }
 }
 
@@ -647,9 +662,16 @@ hipError_t resident_groups_of(const void* kern, int threads, size_t lds, int* ou
 
 namespace {
 
+// Register stages per wave.  Two (one unit in flight while one computes).
+// A third was measured on the 32-row, 256-element-stage kernel: its extra
+// registers spill, and the spill code's waits on in-flight loads cost more
+// than the deeper prefetch gained.
+template <int MB, int NBW, int KSUB, bool SL>
+constexpr int register_stages() { return 2; }
+
 template <int MB, int NBW, int KSUB, int WAVES, bool SL, bool PK = false>
 hipError_t launch_tile(const GemmArgs& p, hipStream_t stream) {
-  auto kern = k_grouped_gemm<MB, NBW, KSUB, WAVES, SL, PK>;
+  auto kern = k_grouped_gemm<MB, NBW, KSUB, WAVES, SL, PK, register_stages<MB, NBW, KSUB, SL>()>;
   const size_t lds = worklist_bytes(p.num_experts) + (SL ? (size_t)WAVES * scale_lds_per_wave<NBW>() : 0);
   int resident = 0;
   hipError_t err = resident_groups(kern, WAVES * 64, lds, &resident);
