@@ -36,11 +36,11 @@ namespace {
 constexpr int kThreads = 256;
 
 // Sixteen consecutive input elements as floats (BF16 widens exactly).
-template <int DT>
-__device__ __forceinline__ void load_block16(const void* x, int64_t row, int64_t ld_x, int64_t b,
+template <int DT, typename I>
+__device__ __forceinline__ void load_block16(const void* x, I row, int64_t ld_x, I b,
                                              float (&v)[16]) {
   if (DT == 0) {  // BF16
-    const uint8_t* p = reinterpret_cast<const uint8_t*>(x) + (row * ld_x + b * 16) * 2;
+    const uint8_t* p = reinterpret_cast<const uint8_t*>(x) + ((int64_t)row * ld_x + (int64_t)b * 16) * 2;
     u32x4_t w0 = load_16B(p), w1 = load_16B(p + 16);
     uint32_t w[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
 #pragma unroll
@@ -49,7 +49,7 @@ __device__ __forceinline__ void load_block16(const void* x, int64_t row, int64_t
       v[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
     }
   } else {  // FP32
-    const uint8_t* p = reinterpret_cast<const uint8_t*>(x) + (row * ld_x + b * 16) * 4;
+    const uint8_t* p = reinterpret_cast<const uint8_t*>(x) + ((int64_t)row * ld_x + (int64_t)b * 16) * 4;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const u32x4_t w = load_16B(p + 16 * j);
@@ -72,19 +72,34 @@ __global__ void k_set_one(float* ts) {
   if (blockIdx.x == 0 && threadIdx.x == 0) *ts = 1.0f;
 }
 
-template <int DT>
+// Blocks per thread per iteration of the amax pass: all their loads are in
+// flight before the reduction.
+constexpr int kAmaxBlocks = 4;
+
+// I: the index type (32-bit whenever rows * k/16 fits, which avoids 64-bit
+// division in the index arithmetic).
+template <int DT, typename I>
 __global__ __launch_bounds__(kThreads) void k_amax(const void* x, int64_t rows, int64_t k,
                                                    int64_t ld_x, float* ts) {
   __shared__ float wave_max[kThreads / 64];
-  const int64_t nb = k / 16;
-  const int64_t total = rows * nb;
+  const I nb = (I)(k / 16);
+  const I total = (I)rows * nb;
+  const I stride = (I)gridDim.x * kThreads;
   float m = 0.0f;
-  for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < total;
-       blk += (int64_t)gridDim.x * kThreads) {
-    float v[16];
-    load_block16<DT>(x, blk / nb, ld_x, blk % nb, v);
+  for (I blk = (I)blockIdx.x * kThreads + threadIdx.x; blk < total; blk += kAmaxBlocks * stride) {
+    float v[kAmaxBlocks][16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+    for (int j = 0; j < kAmaxBlocks; ++j) {
+      // Past the end, re-read the last block: a duplicate leaves the max as it is.
+      I bj = blk + (I)j * stride;
+      bj = bj < total ? bj : total - 1;
+      const I row = bj / nb;
+      load_block16<DT, I>(x, row, ld_x, bj - row * nb, v[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < kAmaxBlocks; ++j)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[j][i]));
   }
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
@@ -110,7 +125,7 @@ __device__ __forceinline__ float tensor_scale_of(const float* ts) {
   return __builtin_bit_cast(uint32_t, t) == kNoAmax ? 1.0f : t;
 }
 
-template <int DT, bool DYN>
+template <int DT, bool DYN, typename I>
 __global__ __launch_bounds__(kThreads) void k_quantize(const void* x, int64_t rows, int64_t k,
                                                        int64_t ld_x, uint8_t* q, uint8_t* sf,
                                                        const float* ts) {
@@ -120,13 +135,12 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const void* x, int64_t ro
   if (DYN && blockIdx.x == 0 && threadIdx.x == 0 && g == 1.0f)
     *const_cast<float*>(ts) = 1.0f;
   const float six_g = 6.0f * g;
-  const int64_t nb = k / 16;
-  const int64_t total = rows * nb;
-  for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < total;
-       blk += (int64_t)gridDim.x * kThreads) {
-    const int64_t row = blk / nb, b = blk % nb;
+  const I nb = (I)(k / 16);
+  const I total = (I)rows * nb;
+  for (I blk = (I)blockIdx.x * kThreads + threadIdx.x; blk < total; blk += (I)gridDim.x * kThreads) {
+    const I row = blk / nb, b = blk - row * nb;
     float v[16];
-    load_block16<DT>(x, row, ld_x, b, v);
+    load_block16<DT, I>(x, row, ld_x, b, v);
     float amax_b = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) amax_b = fmaxf(amax_b, fabsf(v[i]));
@@ -146,13 +160,14 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const void* x, int64_t ro
         packed[i >> 2] |= c << (8 * (i & 3));
       }
     }
-    *reinterpret_cast<u32x2_t*>(q + row * (k / 2) + b * 8) = u32x2_t{packed[0], packed[1]};
-    sf[row * nb + b] = (uint8_t)sfb;
+    *reinterpret_cast<u32x2_t*>(q + (int64_t)row * (k / 2) + (int64_t)b * 8) =
+        u32x2_t{packed[0], packed[1]};
+    sf[(int64_t)row * nb + b] = (uint8_t)sfb;
   }
 }
 
 
-template <int DT>
+template <int DT, typename I>
 hipError_t launch_dt(const void* x, int64_t rows, int64_t k, int64_t ld_x, uint8_t* q, uint8_t* sf,
                      float* ts, int dynamic, hipStream_t stream) {
   const int64_t total = rows * (k / 16);
@@ -160,20 +175,33 @@ hipError_t launch_dt(const void* x, int64_t rows, int64_t k, int64_t ld_x, uint8
   const int grid = (int)(want < 65536 ? (want > 0 ? want : 1) : 65536);
   if (dynamic) {
     if (total > 0) {
-      // Few workgroups with one atomic each: the reduction target is one word.
-      const int agrid = grid < 256 ? grid : 256;
+      // One atomic per workgroup on a single word: size the amax grid so each
+      // thread covers kAmaxBlocks blocks per pass, at most 1024 workgroups.
+      const int64_t awant = (want + kAmaxBlocks - 1) / kAmaxBlocks;
+      const int agrid = (int)(awant < 1024 ? awant : 1024);
       hipLaunchKernelGGL(k_amax_reset, dim3(1), dim3(64), 0, stream, ts);
-      hipLaunchKernelGGL((k_amax<DT>), dim3(agrid), dim3(kThreads), 0, stream, x, rows, k, ld_x, ts);
-      hipLaunchKernelGGL((k_quantize<DT, true>), dim3(grid), dim3(kThreads), 0, stream, x, rows, k,
-                         ld_x, q, sf, (const float*)ts);
+      hipLaunchKernelGGL((k_amax<DT, I>), dim3(agrid), dim3(kThreads), 0, stream, x, rows, k, ld_x, ts);
+      hipLaunchKernelGGL((k_quantize<DT, true, I>), dim3(grid), dim3(kThreads), 0, stream, x, rows,
+                         k, ld_x, q, sf, (const float*)ts);
     } else {
       hipLaunchKernelGGL(k_set_one, dim3(1), dim3(64), 0, stream, ts);
     }
   } else if (total > 0) {
-    hipLaunchKernelGGL((k_quantize<DT, false>), dim3(grid), dim3(kThreads), 0, stream, x, rows, k,
-                       ld_x, q, sf, (const float*)ts);
+    hipLaunchKernelGGL((k_quantize<DT, false, I>), dim3(grid), dim3(kThreads), 0, stream, x, rows,
+                       k, ld_x, q, sf, (const float*)ts);
   }
   return hipGetLastError();
+}
+
+// 32-bit block indices when every index (including one stride past the last
+// block) fits, 64-bit otherwise.
+template <int DT>
+hipError_t launch_idx(const void* x, int64_t rows, int64_t k, int64_t ld_x, uint8_t* q, uint8_t* sf,
+                      float* ts, int dynamic, hipStream_t stream) {
+  const int64_t total = rows * (k / 16);
+  const int64_t reach = total + (int64_t)kAmaxBlocks * 1024 * kThreads + 65536LL * kThreads;
+  if (reach < INT32_MAX) return launch_dt<DT, int32_t>(x, rows, k, ld_x, q, sf, ts, dynamic, stream);
+  return launch_dt<DT, int64_t>(x, rows, k, ld_x, q, sf, ts, dynamic, stream);
 }
 
 }  // namespace
@@ -181,8 +209,8 @@ hipError_t launch_dt(const void* x, int64_t rows, int64_t k, int64_t ld_x, uint8
 hipError_t launch_quantize(const void* x, int in_dtype, int64_t rows, int64_t k, int64_t ld_x,
                            uint8_t* q, uint8_t* sf, float* tensor_scale, int dynamic,
                            hipStream_t stream) {
-  if (in_dtype == 0) return launch_dt<0>(x, rows, k, ld_x, q, sf, tensor_scale, dynamic, stream);
-  return launch_dt<1>(x, rows, k, ld_x, q, sf, tensor_scale, dynamic, stream);
+  if (in_dtype == 0) return launch_idx<0>(x, rows, k, ld_x, q, sf, tensor_scale, dynamic, stream);
+  return launch_idx<1>(x, rows, k, ld_x, q, sf, tensor_scale, dynamic, stream);
 }
 
 }  // namespace moe_fp4
