@@ -399,16 +399,74 @@ template <int MB, int NBW>
 struct PendingStores {
   u32x2_t data[NBW][MB];
   uint32_t voff[MB];
+  u32x4_t rows[2 * MB];  // staged epilogue: 8 rows x 128 bytes per store
+  uint32_t rvoff;
 };
 
-template <int MB, int NBW>
+template <int MB, int NBW, bool STAGED>
 __device__ __forceinline__ void hold_stores(const PendingStores<MB, NBW>& ps) {
+  if constexpr (STAGED) {
+    asm volatile("" ::"v"(ps.rvoff));
 #pragma unroll
-  for (int ib = 0; ib < MB; ++ib) {
-    asm volatile("" ::"v"(ps.voff[ib]));
+    for (int k = 0; k < 2 * MB; ++k) asm volatile("" ::"v"(ps.rows[k]));
+  } else {
 #pragma unroll
-    for (int jb = 0; jb < NBW; ++jb) asm volatile("" ::"v"(ps.data[jb][ib]));
+    for (int ib = 0; ib < MB; ++ib) {
+      asm volatile("" ::"v"(ps.voff[ib]));
+#pragma unroll
+      for (int jb = 0; jb < NBW; ++jb) asm volatile("" ::"v"(ps.data[jb][ib]));
+    }
   }
+}
+
+// LDS bytes of a wave's output tile for the staged epilogue: 16*MB rows of
+// 32*NBW bytes, padded by 16 bytes per row against bank conflicts.
+template <int MB, int NBW>
+constexpr int out_tile_pitch() { return 32 * NBW + 16; }
+template <int MB, int NBW>
+constexpr int out_tile_bytes() { return 16 * MB * out_tile_pitch<MB, NBW>(); }
+
+// Staged BF16 store of a finished 64-column item: the wave writes its tile to
+// LDS in the accumulator layout (lane (c, g): row 16*ib + c, columns 16*jb +
+// 4g .. +3), reads it back row-major (lane l: row 8k + l/8, columns 8*(l%8)
+// .. +7) and stores 16 bytes per lane, so every store instruction writes 8
+// whole 128-byte row segments instead of 16 rows x 32 bytes.  A wave's LDS
+// operations execute in order, so no barrier is needed, and the next item's
+// writes cannot overtake these reads.  Rows past the expert's end fall
+// outside the store resource; a column chunk past n gets an out-of-range
+// offset.
+template <int MB, int NBW>
+__device__ __forceinline__ void epilogue_staged(float4_t (&acc)[NBW][MB], const ItemPos& it,
+                                                int lane, const GemmArgs& p,
+                                                PendingStores<MB, NBW>& ps, uint8_t* tile) {
+  static_assert(NBW == 4, "row segments of 64 columns");
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  constexpr int kPitch = out_tile_pitch<MB, NBW>();
+  const int c = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int jb = 0; jb < NBW; ++jb) {
+#pragma unroll
+    for (int ib = 0; ib < MB; ++ib) {
+      const float4_t v = acc[jb][ib];
+      const bf16x4_t b = {(__bf16)(v[0] * it.alpha), (__bf16)(v[1] * it.alpha),
+                          (__bf16)(v[2] * it.alpha), (__bf16)(v[3] * it.alpha)};
+      *reinterpret_cast<u32x2_t*>(tile + (16 * ib + c) * kPitch + 32 * jb + 8 * g) =
+          __builtin_bit_cast(u32x2_t, b);
+      acc[jb][ib] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+  }
+  const int32_t ldo = (int32_t)p.ldo;
+  const rsrc_t o = make_rsrc(p.out + (int64_t)it.row0 * ldo,
+                             (uint32_t)((int64_t)it.rows_valid * ldo * 2));
+  const int r8 = lane >> 3, q = lane & 7;
+  const bool col_ok = it.n0 + 8 * q < (int32_t)p.n;
+  ps.rvoff = col_ok ? (uint32_t)((r8 * ldo + it.n0 + 8 * q) * 2) : kOutOfRange;
+#pragma unroll
+  for (int k = 0; k < 2 * MB; ++k)
+    ps.rows[k] = *reinterpret_cast<const u32x4_t*>(tile + (8 * k + r8) * kPitch + 16 * q);
+#pragma unroll
+  for (int k = 0; k < 2 * MB; ++k)
+    __builtin_amdgcn_raw_buffer_store_b128(ps.rows[k], o, ps.rvoff, uniform(16 * k * ldo), 0);
 }
 
 // BF16 store of a finished item.  Lane (c, g) holds rows 16*ib + c, columns
@@ -444,14 +502,17 @@ __device__ __forceinline__ void epilogue(float4_t (&acc)[NBW][MB], const ItemPos
   }
 }
 
-// One-row-block tiles with 256-element stages, or 512-element stages whose
-// weight scales come through LDS, fit two wavefronts per SIMD (at most 256
-// registers): ask for that so the allocator does not drift past it.
+// Tiles of one or two row blocks with 256-element stages, and one-row-block
+// tiles with 512-element stages whose weight scales come through LDS, fit two
+// wavefronts per SIMD (at most 256 registers): ask for that, or the allocator
+// drifts past it and halves the wavefronts in flight.
 template <int MB, int NBW, int KSUB, int WAVES, bool SL, bool PK, int R>
 __global__ __launch_bounds__(WAVES * 64)
-__attribute__((amdgpu_waves_per_eu(MB == 1 && (KSUB == 1 || (KSUB == 2 && SL)) ? 2 : 1)))
+__attribute__((amdgpu_waves_per_eu((MB <= 2 && KSUB == 1) || (MB == 1 && KSUB == 2 && SL) ? 2 : 1)))
 void k_grouped_gemm(const GemmArgs p) {
   static_assert(R == 2 || (R == 3 && !SL), "a third register stage only without scale lines");
+  // Kernels without scale lines stage the epilogue through a per-wave LDS tile.
+  constexpr bool STAGED = !SL && NBW == 4;
   static_assert(!PK || NBW == 4, "packed weights are read by 64-column items");
   constexpr int BM = 16 * MB;
   constexpr int NTHR = WAVES * 64;
@@ -498,6 +559,7 @@ void k_grouped_gemm(const GemmArgs p) {
   constexpr int kSpanStages = kSpan / (256 * KSUB);  // stages per span
   constexpr int kBufBytes = 16 * NBW * 128;
   uint8_t* const sl_base = smem + worklist_bytes(E) + (size_t)wave * scale_lds_per_wave<NBW>();
+  uint8_t* const out_tile = smem + worklist_bytes(E) + (size_t)wave * out_tile_bytes<MB, NBW>();
   auto line_copy = [&](int32_t round, int32_t st) -> LineCopy {
     LineCopy lc;
     const bool start = st % kSpanStages == 0;
@@ -567,9 +629,13 @@ void k_grouped_gemm(const GemmArgs p) {
 #pragma unroll
     for (int jb = 0; jb < NBW; ++jb) ps.data[jb][ib] = u32x2_t{0u, 0u};
   }
+  ps.rvoff = 0;
+#pragma unroll
+  for (int k = 0; k < 2 * MB; ++k) ps.rows[k] = u32x4_t{0u, 0u, 0u, 0u};
   auto retire = [&](const ItemPos& it) {
     if (++cp_st == nst) {
-      epilogue<MB, NBW>(acc, it, c, g, p, ps);
+      if constexpr (STAGED) epilogue_staged<MB, NBW>(acc, it, lane, p, ps, out_tile);
+      else epilogue<MB, NBW>(acc, it, c, g, p, ps);
       cp_st = 0;
       ++cp_round;
     }
@@ -623,7 +689,7 @@ void k_grouped_gemm(const GemmArgs p) {
       stage_scales(s[r], wsd);
       compute_stage<MB, NBW, KSUB, SL>(s[r], wsd, pos[r].rows_valid, acc);
       hold<MB, NBW>(l[r]);
-      if constexpr (!SL) hold_stores<MB, NBW>(ps);
+      if constexpr (!SL) hold_stores<MB, NBW, STAGED>(ps);
       retire(pos[r]);
       done = u + r + 1 >= units;
     }
@@ -672,7 +738,9 @@ constexpr int register_stages() { return 2; }
 template <int MB, int NBW, int KSUB, int WAVES, bool SL, bool PK = false>
 hipError_t launch_tile(const GemmArgs& p, hipStream_t stream) {
   auto kern = k_grouped_gemm<MB, NBW, KSUB, WAVES, SL, PK, register_stages<MB, NBW, KSUB, SL>()>;
-  const size_t lds = worklist_bytes(p.num_experts) + (SL ? (size_t)WAVES * scale_lds_per_wave<NBW>() : 0);
+  const size_t lds = worklist_bytes(p.num_experts) +
+                     (SL ? (size_t)WAVES * scale_lds_per_wave<NBW>()
+                         : (NBW == 4 ? (size_t)WAVES * out_tile_bytes<MB, NBW>() : 0));
   int resident = 0;
   hipError_t err = resident_groups(kern, WAVES * 64, lds, &resident);
   if (err != hipSuccess) return err;
@@ -744,6 +812,7 @@ int64_t gemm_lds_bytes(const GemmTile& t, int32_t num_experts) {
   if (t.tiled) return (int64_t)tiled_lds(num_experts) + 16;
   int64_t b = (int64_t)worklist_bytes(num_experts) + (int64_t)sizeof(int32_t) * t.waves;
   if (t.lds_scales) b += (int64_t)t.waves * (2 * 16 * 16 * t.n_blocks * 8 + 1024);
+  else if (t.n_blocks == 4) b += (int64_t)t.waves * 16 * t.m_blocks * (32 * t.n_blocks + 16);
   return b;
 }
 
