@@ -235,3 +235,47 @@ def row_error(got_bf16_bits: np.ndarray, ref_bf16_bits: np.ndarray, R: np.ndarra
     safe = np.where(norm > 0, norm, 1.0)
     err = np.where(norm > 0, diff / safe, np.where(diff > 0, np.inf, 0.0))
     return err, norm
+
+
+def combine(R: np.ndarray, out_token: np.ndarray, row_weight: np.ndarray, num_tokens: int,
+            init: np.ndarray | None = None) -> np.ndarray:
+    """MoE finalize step: every routed row's GEMM result, times the row's routing
+    weight, summed into its token's output row.
+
+    The pages name the epilogue that performs the final output write FINALIZE
+    ("Peering into the CUTLASS Kernel", section "Input Knowledge Required", item 5);
+    in the Mixture-of-Experts down projection that write is read here as the
+    routing-weighted sum of a token's expert rows (the step after the plain store
+    of the grouped GEMM):
+
+        out[t][j] = init[t][j] + sum over rows r with out_token[r] = t of
+                    row_weight[r] * R[r][j]
+
+    R float64 [m_total][n] (the exact grouped-GEMM result, unrounded), out_token int
+    [m_total] in [0, num_tokens), row_weight float32 [m_total]; init float [num_tokens][n]
+    or None (zeros).  Evaluated in FP64.  Returns float64 [num_tokens][n].
+    """
+    R = np.asarray(R, dtype=np.float64)
+    out_token = np.asarray(out_token, dtype=np.int64)
+    row_weight = np.asarray(row_weight, dtype=np.float32).astype(np.float64)
+    if R.ndim != 2 or out_token.shape != (R.shape[0],) or row_weight.shape != (R.shape[0],):
+        raise ValueError("combine: R [m][n], out_token [m], row_weight [m]")
+    if np.any(out_token < 0) or np.any(out_token >= num_tokens):
+        raise ValueError("combine: out_token outside [0, num_tokens)")
+    out = (np.zeros((num_tokens, R.shape[1])) if init is None
+           else np.array(init, dtype=np.float64, copy=True))
+    np.add.at(out, out_token, row_weight[:, None] * R)
+    return out
+
+
+def token_row_error(got: np.ndarray, ref: np.ndarray):
+    """Per-row relative L2 error of an FP32 token-order result against the FP64
+    reference: err[t] = ||got[t] - ref[t]||_2 / ||ref[t]||_2; 0 when both rows are zero,
+    inf when the reference row is zero but the result is not.  Returns (err, ||ref[t]||)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    diff = np.linalg.norm(got - ref, axis=1)
+    norm = np.linalg.norm(ref, axis=1)
+    safe = np.where(norm > 0, norm, 1.0)
+    err = np.where(norm > 0, diff / safe, np.where(diff > 0, np.inf, 0.0))
+    return err, norm
