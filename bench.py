@@ -45,7 +45,7 @@ F16_PEAK_TFLOPS = 2516.6        # dense FP16 MFMA, AMD published
 ROTATE_BYTES = 1.0e9            # weight bytes cycled through between reuses
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_grouped_gemm.txt")
 GEMM_SOURCES = [os.path.join(ROOT, "block_scaled_fp4_05_amd", "csrc", f)
-                for f in ("grouped_gemm.hip", "gemm_common.h", "fp4_device.h")]
+                for f in ("grouped_gemm_kernel.h", "grouped_gemm.hip", "gemm_common.h", "fp4_device.h")]
 
 
 def log(msg):

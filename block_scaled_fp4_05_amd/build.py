@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_fp4.so")
 SOURCES = ["api.cpp", "quantize.hip", "grouped_gemm.hip", "grouped_gemm_tiled.hip", "pack.hip"]
-HEADERS = ["fp4_device.h", "gemm_common.h", "launch.h"]
+HEADERS = ["fp4_device.h", "gemm_common.h", "grouped_gemm_kernel.h", "launch.h"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
