@@ -9,7 +9,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_fp4.so")
-SOURCES = ["api.cpp", "quantize.hip", "grouped_gemm.hip", "grouped_gemm_tiled.hip", "pack.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "grouped_gemm.hip", "grouped_gemm_finalize.hip",
+           "grouped_gemm_tiled.hip", "pack.hip"]
 HEADERS = ["fp4_device.h", "gemm_common.h", "grouped_gemm_kernel.h", "launch.h"]
 
 HIPCC_FLAGS = [

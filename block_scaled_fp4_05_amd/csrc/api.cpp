@@ -133,7 +133,7 @@ int grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const float* a_scale, 
       (t.n_blocks != 4 || t.k_sub != moe_fp4::packed_granule(k) / moe_fp4::kKStep))
     return MOE_FP4_ERR_UNSUPPORTED;
   if (m_total == 0) return MOE_FP4_OK;
-  GemmArgs p;
+  GemmArgs p = {};
   p.a_q = a_q;
   p.a_sf = a_sf;
   p.a_scale = a_scale;
@@ -152,6 +152,68 @@ int grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const float* a_scale, 
   p.n_tiles = (int32_t)((n + 16 * t.n_blocks - 1) / (16 * t.n_blocks));
   p.w_packed = packed ? 1 : 0;
   hipError_t err = moe_fp4::launch_grouped_gemm(p, t, reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? MOE_FP4_OK : MOE_FP4_ERR_HIP;
+}
+
+int grouped_gemm_finalize(const uint8_t* a_q, const uint8_t* a_sf, const float* a_scale,
+                          int64_t a_rows, const int32_t* a_row_index, const uint8_t* w_q,
+                          const uint8_t* w_sf, const float* w_scale, int w_packed,
+                          const int32_t* expert_offsets, int32_t num_experts, int64_t m_total,
+                          int64_t n, int64_t k, const int32_t* out_token,
+                          const float* row_weight, float* out, int64_t ldo, int64_t num_tokens,
+                          void* stream) {
+  if (!a_q || !a_sf || !a_scale || !w_q || !w_sf || !w_scale || !expert_offsets || !out ||
+      !out_token || !row_weight)
+    return MOE_FP4_ERR_NULL;
+  if (w_packed != 0 && w_packed != 1) return MOE_FP4_ERR_ARG;
+  if (num_experts < 1 || m_total < 0 || n < 1 || k < 1 || ldo < n || a_rows < 0 || num_tokens < 1)
+    return MOE_FP4_ERR_SHAPE;
+  if (!a_row_index && a_rows < m_total) return MOE_FP4_ERR_SHAPE;
+  if (m_total > 0 && a_rows < 1) return MOE_FP4_ERR_SHAPE;
+  const int s = check_gemm_shape(num_experts, m_total, n, k);
+  if (s != MOE_FP4_OK) return s;
+  if (!aligned(a_q, 16) || !aligned(a_sf, 16) || !aligned(w_q, 16) || !aligned(w_sf, 16) ||
+      !aligned(out, 4) || !aligned(a_scale, 4) || !aligned(w_scale, 4) ||
+      !aligned(expert_offsets, 4) || (a_row_index && !aligned(a_row_index, 4)) ||
+      !aligned(out_token, 4) || !aligned(row_weight, 4))
+    return MOE_FP4_ERR_ALIGN;
+  if (a_rows * (k / 2) > (int64_t)INT32_MAX - 4096) return MOE_FP4_ERR_UNSUPPORTED;
+  // The token rows are addressed with 32-bit byte offsets.
+  if (num_tokens > (int64_t)INT32_MAX / 4 || num_tokens * ldo * 4 > (int64_t)INT32_MAX - 4096)
+    return MOE_FP4_ERR_UNSUPPORTED;
+  GemmTile t = moe_fp4::choose_tile(num_experts, m_total, n, k, getenv("MOE_FP4_TILE"));
+  // The finalize epilogue runs in the per-wave kernel with 64-column items;
+  // experts large enough for the workgroup tile take four row blocks per item.
+  if (t.tiled) t = GemmTile{4, 4, 4, k % 512 == 0 ? 2 : 1, k % 2048 == 0 ? 1 : 0, 0};
+  if (t.n_blocks != 4 || t.k_sub > 2) return MOE_FP4_ERR_UNSUPPORTED;
+  if (w_packed && t.k_sub != moe_fp4::packed_granule(k) / moe_fp4::kKStep)
+    return MOE_FP4_ERR_UNSUPPORTED;
+  if (m_total == 0) return MOE_FP4_OK;
+  GemmArgs p = {};
+  p.a_q = a_q;
+  p.a_sf = a_sf;
+  p.a_scale = a_scale;
+  p.a_row_index = a_row_index;
+  p.w_q = w_q;
+  p.w_sf = w_sf;
+  p.w_scale = w_scale;
+  p.offsets = expert_offsets;
+  p.out = nullptr;
+  p.a_rows = a_rows;
+  p.m_total = m_total;
+  p.n = n;
+  p.k = k;
+  p.ldo = n;
+  p.num_experts = num_experts;
+  p.n_tiles = (int32_t)((n + 63) / 64);
+  p.w_packed = w_packed;
+  p.out_token = out_token;
+  p.row_weight = row_weight;
+  p.fin_out = out;
+  p.fin_ldo = ldo;
+  p.num_tokens = num_tokens;
+  hipError_t err =
+      moe_fp4::launch_grouped_gemm_finalize(p, t, reinterpret_cast<hipStream_t>(stream));
   return err == hipSuccess ? MOE_FP4_OK : MOE_FP4_ERR_HIP;
 }
 
@@ -192,6 +254,18 @@ int moe_grouped_gemm_fp4_packed(const uint8_t* a_q, const uint8_t* a_sf, const f
                                 uint16_t* out, int64_t ldo, void* stream) {
   return grouped_gemm(a_q, a_sf, a_scale, a_rows, a_row_index, w_packed, w_sf, w_scale,
                       expert_offsets, num_experts, m_total, n, k, out, ldo, stream, true);
+}
+
+int moe_grouped_gemm_fp4_finalize(const uint8_t* a_q, const uint8_t* a_sf, const float* a_scale,
+                                  int64_t a_rows, const int32_t* a_row_index,
+                                  const uint8_t* w_q, const uint8_t* w_sf, const float* w_scale,
+                                  int w_packed, const int32_t* expert_offsets,
+                                  int32_t num_experts, int64_t m_total, int64_t n, int64_t k,
+                                  const int32_t* out_token, const float* row_weight, float* out,
+                                  int64_t ldo, int64_t num_tokens, void* stream) {
+  return grouped_gemm_finalize(a_q, a_sf, a_scale, a_rows, a_row_index, w_q, w_sf, w_scale,
+                               w_packed, expert_offsets, num_experts, m_total, n, k, out_token,
+                               row_weight, out, ldo, num_tokens, stream);
 }
 
 int moe_fp4_pack_weights(const uint8_t* w_q, uint8_t* w_packed, int32_t num_experts,

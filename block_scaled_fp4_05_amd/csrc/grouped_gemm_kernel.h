@@ -502,17 +502,59 @@ __device__ __forceinline__ void epilogue(float4_t (&acc)[NBW][MB], const ItemPos
   }
 }
 
+// Finalize epilogue: routed row r of the item adds row_weight[r] * alpha *
+// acc into FP32 row out_token[r] of fin_out, one atomic add per element, so the
+// top-k rows of a token, which belong to different experts and therefore to
+// different work items, meet in token order without a BF16 round trip
+// ("Peering into the CUTLASS Kernel", section "Input Knowledge Required", item
+// 5: the epilogue that performs the final output write).  The order in which a
+// token's rows arrive is not fixed.  Lane (c, g) holds rows 16*ib + c, columns
+// 16*jb + 4g .. +3; rows past the expert's end, and tokens outside
+// [0, num_tokens), get an out-of-range offset; a column block past n
+// (uniform) is skipped.
+template <int MB, int NBW>
+__device__ __forceinline__ void epilogue_finalize(float4_t (&acc)[NBW][MB], const ItemPos& it,
+                                                  int c, int g, const GemmArgs& p,
+                                                  const int32_t (&tok)[MB],
+                                                  const float (&wt)[MB]) {
+  const int32_t ldt = (int32_t)p.fin_ldo, ntok = (int32_t)p.num_tokens;
+  const rsrc_t o = make_rsrc(p.fin_out, (uint32_t)((int64_t)ntok * ldt * 4));
+  uint32_t base[MB];
+#pragma unroll
+  for (int ib = 0; ib < MB; ++ib) {
+    const bool ok = 16 * ib + c < it.rows_valid && tok[ib] >= 0 && tok[ib] < ntok;
+    base[ib] = ok ? (uint32_t)(tok[ib] * ldt + it.n0 + 4 * g) * 4u : kOutOfRange;
+  }
+#pragma unroll
+  for (int jb = 0; jb < NBW; ++jb) {
+    if (it.n0 + 16 * jb < (int32_t)p.n) {
+#pragma unroll
+      for (int ib = 0; ib < MB; ++ib) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = (acc[jb][ib][i] * it.alpha) * wt[ib];
+          __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, o, base[ib] + 64u * jb + 4u * i, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int ib = 0; ib < MB; ++ib) acc[jb][ib] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+}
+
 // Tiles of one or two row blocks with 256-element stages, and one-row-block
 // tiles with 512-element stages whose weight scales come through LDS, fit two
 // wavefronts per SIMD (at most 256 registers): ask for that, or the allocator
 // drifts past it and halves the wavefronts in flight.
-template <int MB, int NBW, int KSUB, int WAVES, bool SL, bool PK, int R>
+template <int MB, int NBW, int KSUB, int WAVES, bool SL, bool PK, int R, bool FIN>
 __global__ __launch_bounds__(WAVES * 64)
 __attribute__((amdgpu_waves_per_eu((MB <= 2 && KSUB == 1) || (MB == 1 && KSUB == 2 && SL) ? 2 : 1)))
 void k_grouped_gemm(const GemmArgs p) {
   static_assert(R == 2 || (R == 3 && !SL), "a third register stage only without scale lines");
-  // Kernels without scale lines stage the epilogue through a per-wave LDS tile.
-  constexpr bool STAGED = !SL && NBW == 4;
+  // Kernels without scale lines stage the epilogue through a per-wave LDS tile
+  // (the finalize epilogue adds in place and needs none).
+  constexpr bool STAGED = !SL && NBW == 4 && !FIN;
+  static_assert(!FIN || NBW == 4, "finalize kernels use 64-column items");
   static_assert(!PK || NBW == 4, "packed weights are read by 64-column items");
   constexpr int BM = 16 * MB;
   constexpr int NTHR = WAVES * 64;
@@ -593,6 +635,22 @@ void k_grouped_gemm(const GemmArgs p) {
 #pragma unroll
   for (int ib = 0; ib < MB; ++ib) nrow[ib] = row_index_load(idx_rs, ld_pos, ib, c);
   item_loads<MB, NBW, KSUB, PK>(ld_pos, p, lane, nrow, l[0]);
+  // Finalize: each row's destination token and routing weight, fetched like
+  // the row-index entries (ntok/nwt: of the item being started, then of nx)
+  // and carried per register stage to the item's epilogue (ftok/fwt).
+  const rsrc_t tok_rs = make_rsrc(p.out_token, FIN ? (uint32_t)(4 * m_total) : 0u);
+  const rsrc_t wt_rs = make_rsrc(p.row_weight, FIN ? (uint32_t)(4 * m_total) : 0u);
+  int32_t ntok[MB], ftok[R][MB];
+  float nwt[MB], fwt[R][MB];
+  if constexpr (FIN) {
+#pragma unroll
+    for (int ib = 0; ib < MB; ++ib) {
+      ntok[ib] = (int32_t)row_index_load(tok_rs, ld_pos, ib, c);
+      nwt[ib] = __builtin_bit_cast(float, row_index_load(wt_rs, ld_pos, ib, c));
+      ftok[0][ib] = ntok[ib];
+      fwt[0][ib] = nwt[ib];
+    }
+  }
   // nx: the item after ld's, located a stage or more before it is needed
   // (the last item repeats itself; that copy is never used).
   auto locate_next = [&](int32_t round) {
@@ -607,20 +665,28 @@ void k_grouped_gemm(const GemmArgs p) {
   auto prefetch_rows = [&]() {
 #pragma unroll
     for (int ib = 0; ib < MB; ++ib) nrow[ib] = row_index_load(idx_rs, nx, ib, c);
+    if constexpr (FIN) {
+#pragma unroll
+      for (int ib = 0; ib < MB; ++ib) {
+        ntok[ib] = (int32_t)row_index_load(tok_rs, nx, ib, c);
+        nwt[ib] = __builtin_bit_cast(float, row_index_load(wt_rs, nx, ib, c));
+      }
+    }
   };
   prefetch_rows();
   // Move the load position to the next unit: a new item (already located)
   // gets its lane offsets in dst, otherwise dst takes src's offsets.
-  auto advance = [&](ItemLoads<MB, NBW>& dst, const ItemLoads<MB, NBW>& src) {
+  auto advance = [&](ItemLoads<MB, NBW>& dst, const ItemLoads<MB, NBW>& src) -> bool {
     if (++ld_st == nst) {
       ld_st = 0;
       ++ld_round;
       ld_pos = nx;
       item_loads<MB, NBW, KSUB, PK>(ld_pos, p, lane, nrow, dst);
       locate_next(ld_round);
-    } else {
-      dst = src;
+      return true;
     }
+    dst = src;
+    return false;
   };
   PendingStores<MB, NBW> ps;
 #pragma unroll
@@ -632,9 +698,10 @@ void k_grouped_gemm(const GemmArgs p) {
   ps.rvoff = 0;
 #pragma unroll
   for (int k = 0; k < 2 * MB; ++k) ps.rows[k] = u32x4_t{0u, 0u, 0u, 0u};
-  auto retire = [&](const ItemPos& it) {
+  auto retire = [&](const ItemPos& it, const int32_t (&tok)[MB], const float (&wt)[MB]) {
     if (++cp_st == nst) {
-      if constexpr (STAGED) epilogue_staged<MB, NBW>(acc, it, lane, p, ps, out_tile);
+      if constexpr (FIN) epilogue_finalize<MB, NBW>(acc, it, c, g, p, tok, wt);
+      else if constexpr (STAGED) epilogue_staged<MB, NBW>(acc, it, lane, p, ps, out_tile);
       else epilogue<MB, NBW>(acc, it, c, g, p, ps);
       cp_st = 0;
       ++cp_round;
@@ -662,8 +729,16 @@ void k_grouped_gemm(const GemmArgs p) {
   Stage<MB, NBW, KSUB> s[R];
   auto issue = [&](int to, int from, int32_t v) {
     const bool more = v < units;
-    if (more) advance(l[to], l[from]); else l[to] = nowhere<MB, NBW>(l[from]);
+    bool fresh = false;
+    if (more) fresh = advance(l[to], l[from]); else l[to] = nowhere<MB, NBW>(l[from]);
     pos[to] = ld_pos;
+    if constexpr (FIN) {
+#pragma unroll
+      for (int ib = 0; ib < MB; ++ib) {
+        ftok[to][ib] = fresh ? ntok[ib] : ftok[from][ib];
+        fwt[to][ib] = fresh ? nwt[ib] : fwt[from][ib];
+      }
+    }
     prefetch_rows();
     issue_loads<MB, NBW, KSUB, SL, PK>(s[to], l[to], a_rs, as_rs, ld_st,
                                        more ? line_copy(ld_round, ld_st)
@@ -690,7 +765,7 @@ void k_grouped_gemm(const GemmArgs p) {
       compute_stage<MB, NBW, KSUB, SL>(s[r], wsd, pos[r].rows_valid, acc);
       hold<MB, NBW>(l[r]);
       if constexpr (!SL) hold_stores<MB, NBW, STAGED>(ps);
-      retire(pos[r]);
+      retire(pos[r], ftok[r], fwt[r]);
       done = u + r + 1 >= units;
     }
   }
@@ -704,12 +779,12 @@ void k_grouped_gemm(const GemmArgs p) {
 template <int MB, int NBW, int KSUB, bool SL>
 constexpr int register_stages() { return 2; }
 
-template <int MB, int NBW, int KSUB, int WAVES, bool SL, bool PK = false>
+template <int MB, int NBW, int KSUB, int WAVES, bool SL, bool PK = false, bool FIN = false>
 hipError_t launch_tile(const GemmArgs& p, hipStream_t stream) {
-  auto kern = k_grouped_gemm<MB, NBW, KSUB, WAVES, SL, PK, register_stages<MB, NBW, KSUB, SL>()>;
+  auto kern = k_grouped_gemm<MB, NBW, KSUB, WAVES, SL, PK, register_stages<MB, NBW, KSUB, SL>(), FIN>;
   const size_t lds = worklist_bytes(p.num_experts) +
                      (SL ? (size_t)WAVES * scale_lds_per_wave<NBW>()
-                         : (NBW == 4 ? (size_t)WAVES * out_tile_bytes<MB, NBW>() : 0));
+                         : (NBW == 4 && !FIN ? (size_t)WAVES * out_tile_bytes<MB, NBW>() : 0));
   int resident = 0;
   hipError_t err = resident_groups(kern, WAVES * 64, lds, &resident);
   if (err != hipSuccess) return err;

@@ -64,9 +64,21 @@ struct GemmArgs {
   int32_t num_experts;
   int32_t n_tiles;   // ceil(n / (16 * n_blocks))
   int32_t w_packed;  // w_q is in the packed layout
+  // Finalize epilogue only (moe_grouped_gemm_fp4_finalize): routed row r adds
+  // row_weight[r] * its result into FP32 row out_token[r] of fin_out.
+  const int32_t* out_token;
+  const float* row_weight;
+  float* fin_out;
+  int64_t fin_ldo;
+  int64_t num_tokens;
 };
 
 hipError_t launch_grouped_gemm(const GemmArgs& args, const GemmTile& tile, hipStream_t stream);
+
+// The same GEMM with the finalize epilogue (grouped_gemm_finalize.hip): per-wave
+// kernels with 64-column items only.
+hipError_t launch_grouped_gemm_finalize(const GemmArgs& args, const GemmTile& tile,
+                                        hipStream_t stream);
 
 // Workgroup-tiled kernel (grouped_gemm_tiled.hip): 128 x 128 items, 4 waves.
 hipError_t launch_grouped_gemm_tiled(const GemmArgs& args, hipStream_t stream);

@@ -20,6 +20,7 @@ SCALE_STATIC, SCALE_DYNAMIC = 0, 1
 
 # Every symbol include/moe_fp4.h declares.
 EXPORTED = ("moe_fp4_quantize", "moe_grouped_gemm_fp4", "moe_grouped_gemm_fp4_packed",
+            "moe_grouped_gemm_fp4_finalize",
             "moe_fp4_pack_weights", "moe_fp4_unpack_weights", "moe_grouped_gemm_fp4_plan",
             "moe_fp4_stage_bytes", "moe_fp4_status_string", "moe_fp4_abi_version")
 
@@ -55,6 +56,9 @@ def lib() -> ctypes.CDLL:
     L.moe_grouped_gemm_fp4.restype = i
     L.moe_grouped_gemm_fp4_packed.argtypes = L.moe_grouped_gemm_fp4.argtypes
     L.moe_grouped_gemm_fp4_packed.restype = i
+    L.moe_grouped_gemm_fp4_finalize.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp, i, vp, i32, i64,
+                                                 i64, i64, vp, vp, vp, i64, i64, vp]
+    L.moe_grouped_gemm_fp4_finalize.restype = i
     for f in (L.moe_fp4_pack_weights, L.moe_fp4_unpack_weights):
         f.argtypes = [vp, vp, i32, i64, i64, vp]
         f.restype = i
@@ -195,4 +199,29 @@ def grouped_gemm(a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets, a_row_index=No
             _ptr(w_scale), _ptr(offsets), E, m_total, n, k, _ptr(out), out.stride(0), _stream(stream))
     if st != OK:
         raise MoeFp4Error(st, "moe_grouped_gemm_fp4_packed" if packed else "moe_grouped_gemm_fp4")
+    return out
+
+
+def finalize_raw(*args):
+    """moe_grouped_gemm_fp4_finalize with raw pointers (C argument order); returns the status."""
+    return lib().moe_grouped_gemm_fp4_finalize(*args)
+
+
+def grouped_gemm_finalize(a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets, out_token, row_weight,
+                          out, a_row_index=None, m_total: int | None = None, packed: bool = False,
+                          stream=None):
+    """Grouped GEMM with the finalize epilogue: routed row r adds row_weight[r] times its
+    result into row out_token[r] of `out` (float32 CUDA tensor [num_tokens][ldo],
+    accumulated into).  Other arguments as grouped_gemm.  Returns out."""
+    E, n, kb = w_q.shape
+    k = 2 * kb
+    a_rows = a_q.shape[0]
+    if m_total is None:
+        m_total = a_row_index.shape[0] if a_row_index is not None else a_rows
+    st = lib().moe_grouped_gemm_fp4_finalize(
+        _ptr(a_q), _ptr(a_sf), _ptr(a_scale), a_rows, _ptr(a_row_index), _ptr(w_q), _ptr(w_sf),
+        _ptr(w_scale), 1 if packed else 0, _ptr(offsets), E, m_total, n, k, _ptr(out_token),
+        _ptr(row_weight), _ptr(out), out.stride(0), out.shape[0], _stream(stream))
+    if st != OK:
+        raise MoeFp4Error(st, "moe_grouped_gemm_fp4_finalize")
     return out

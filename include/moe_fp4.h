@@ -207,6 +207,48 @@ int moe_grouped_gemm_fp4_packed(const uint8_t* a_q, const uint8_t* a_sf, const f
                                 int32_t num_experts, int64_t m_total, int64_t n, int64_t k,
                                 uint16_t* out, int64_t ldo, void* stream);
 
+/*
+ * moe_grouped_gemm_fp4_finalize -- the grouped GEMM with the Mixture-of-Experts
+ * finalize step in its epilogue: every routed row's result, times that row's
+ * routing weight, is added into its token's FP32 output row, so the top-k rows
+ * of a token (computed by different experts) are summed in token order without
+ * writing the per-row BF16 result.  The pages name the epilogue that performs
+ * the final output write FINALIZE ("Peering into the CUTLASS Kernel", section
+ * "Input Knowledge Required", item 5); this library reads it, for the down
+ * projection, as this routing-weighted sum.
+ *
+ *     out[out_token[r]][j] += row_weight[r] * a_scale * w_scale[e]
+ *                             * sum_k A(src(r), k) * W(e, j, k)
+ *
+ * for every routed row r of expert e (rows [off[e], off[e+1])) and j < n, with
+ * A, W, src and the exact FP32-accumulated sum as in moe_grouped_gemm_fp4; the
+ * product is rounded to FP32 as fl(fl(acc * fl(a_scale * w_scale[e])) * row_weight[r]).
+ * Arguments as moe_grouped_gemm_fp4 (w_packed: 0 = row-major w_q, 1 = the packed
+ * layout), plus:
+ *   out_token   device, [m_total] int32: destination token of each routed row;
+ *               a row whose token is outside [0, num_tokens) adds nothing.
+ *   row_weight  device, [m_total] float: routing weight of each routed row.
+ *   out         device, [num_tokens][ldo] FP32, accumulated into (+=): zero it for
+ *               the plain sum, or pass a residual stream to add onto it.  4-byte
+ *               aligned, ldo >= n.  Columns >= n are never touched.
+ *   num_tokens  rows of out (>= 1).
+ * The additions into one element run concurrently (FP32 atomic adds), so their
+ * order, and therefore the last bits of the sum, can differ between runs.  The
+ * kernel runs per-wavefront 64-column items (experts of any size; large ones
+ * are not given the workgroup tile).
+ * Errors: as moe_grouped_gemm_fp4, plus NULL (out_token, row_weight), SHAPE
+ * (num_tokens < 1), ALIGN (out_token, row_weight, out not 4-byte aligned), ARG
+ * (w_packed not 0 or 1), UNSUPPORTED (num_tokens * ldo * 4 >= 2^31 - 4096, or a
+ * MOE_FP4_TILE override this epilogue does not run).
+ */
+int moe_grouped_gemm_fp4_finalize(const uint8_t* a_q, const uint8_t* a_sf, const float* a_scale,
+                                  int64_t a_rows, const int32_t* a_row_index,
+                                  const uint8_t* w_q, const uint8_t* w_sf, const float* w_scale,
+                                  int w_packed, const int32_t* expert_offsets,
+                                  int32_t num_experts, int64_t m_total, int64_t n, int64_t k,
+                                  const int32_t* out_token, const float* row_weight, float* out,
+                                  int64_t ldo, int64_t num_tokens, void* stream);
+
 /* Kernel configuration the GEMM picks for a problem (host-only, no GPU call). */
 typedef struct {
   int32_t tile_m;          /* rows of one expert per work item                       */

@@ -193,3 +193,38 @@ def test_packed_layout_definition_is_a_group_preserving_permutation(n, k):
     first = src[:64]
     assert np.array_equal(first[:16] // kb, np.arange(16))
     assert np.array_equal(first[16:32] - first[:16], np.full(16, G // 8))
+
+
+def _gf(**kw):
+    a = dict(a_q=P16, a_sf=P16, a_scale=P16, a_rows=64, idx=None, w_q=P16, w_sf=P16, w_scale=P16,
+             pk=0, off=P16, E=4, m=64, n=64, k=512, tok=P16, wt=P16, out=P16, ldo=64, T=32,
+             stream=None)
+    a.update(kw)
+    return _lib().finalize_raw(a["a_q"], a["a_sf"], a["a_scale"], a["a_rows"], a["idx"], a["w_q"],
+                               a["w_sf"], a["w_scale"], a["pk"], a["off"], a["E"], a["m"], a["n"],
+                               a["k"], a["tok"], a["wt"], a["out"], a["ldo"], a["T"], a["stream"])
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("kw,status", [
+    (dict(tok=None), 1), (dict(wt=None), 1), (dict(out=None), 1), (dict(w_q=None), 1),
+    (dict(pk=2), 6), (dict(T=0), 2), (dict(ldo=32), 2), (dict(E=0), 2), (dict(n=24, ldo=24), 4),
+    (dict(k=320), 4), (dict(out=P16 + 2), 3), (dict(tok=P16 + 2), 3), (dict(wt=P16 + 1), 3),
+    (dict(T=1 << 24, ldo=64), 4),
+])
+def test_finalize_rejects(kw, status):
+    assert _gf(**kw) == status
+
+
+@needs_no_gpu
+def test_finalize_empty_problem_is_a_noop():
+    assert _gf(m=0, a_rows=0) == 0
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("tile,pk", [("16x32", 0), ("32x32x1024", 0), ("16x64x256", 1)])
+def test_finalize_rejects_tiles_it_does_not_run(tile, pk, monkeypatch):
+    # k = 1024: 32-column items and 1024-element stages are not run by the finalize
+    # epilogue; packed weights (512-element granule) need 512-element stages.
+    monkeypatch.setenv("MOE_FP4_TILE", tile)
+    assert _gf(k=1024, pk=pk) == 4
