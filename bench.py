@@ -63,6 +63,9 @@ def parse_args():
     ap.add_argument("--layout", default="packed", choices=("packed", "rowmajor"),
                     help="weight-code layout the GEMM reads (default packed)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--finalize", action="store_true",
+                    help="also time the finalize GEMM (routing-weighted sum into token order) "
+                         "against the plain GEMM plus a separate weighted combine")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a device copy of known size (counter scale factor)")
     return ap.parse_args()
@@ -214,6 +217,98 @@ def measure(prob, steps, warmup):
                 quant_ms=quant_ms, gemm_ms=gemm_ms)
 
 
+def finalize_report(prob, steps):
+    """The MoE finalize step on this workload (each routed row, times a seeded routing
+    weight, summed into its token's row), three ways:
+      fused    moe_grouped_gemm_fp4_finalize (FP32 atomic adds in the GEMM's epilogue)
+               plus zeroing the caller's FP32 token buffer;
+      two-pass the plain GEMM (BF16 rows) followed by moe_fp4_combine (token order, FP32
+               sums, BF16 out);
+      torch    the plain GEMM followed by a weighted index_add (for reference)."""
+    import numpy as np
+    import torch
+    from block_scaled_fp4_05_amd import moe_fp4
+    w = prob.w
+    dev = torch.device("cuda")
+    weight = torch.from_numpy(np.random.default_rng(700).uniform(0.0, 1.0, prob.m_total)
+                              .astype(np.float32)).to(dev)
+    tokens = torch.empty((w.tokens, w.n), dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(steps):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps * 1e3
+
+    def fused(i):
+        w_q, w_sf, w_scale = prob.weights[i % len(prob.weights)]
+        moe_fp4.grouped_gemm_finalize(prob.q, prob.sf, prob.g, w_q, w_sf, w_scale, prob.off,
+                                      prob.idx, weight, tokens, a_row_index=prob.idx,
+                                      m_total=prob.m_total, packed=prob.packed)
+
+    def zero(i):
+        tokens.zero_()
+
+    def plain(i):
+        w_q, w_sf, w_scale = prob.weights[i % len(prob.weights)]
+        moe_fp4.grouped_gemm(prob.q, prob.sf, prob.g, w_q, w_sf, w_scale, prob.off,
+                             a_row_index=prob.idx, out=prob.out, m_total=prob.m_total,
+                             packed=prob.packed)
+
+    idx64 = prob.idx.to(torch.int64)
+
+    def combine(i):
+        tokens.index_add_(0, idx64, prob.out.float() * weight[:, None])
+
+    # Token -> routed rows map (rows are sorted by expert; a token's rows in row order).
+    row_token = prob.row_token.astype(np.int64)
+    order = np.argsort(row_token, kind="stable")
+    topk = w.topk
+    tr_host = np.full((w.tokens, topk), -1, np.int32)
+    counts = np.bincount(row_token, minlength=w.tokens)
+    starts = np.concatenate([[0], np.cumsum(counts)[:-1]])
+    slot = np.arange(len(order)) - np.repeat(starts, counts)
+    tr_host[row_token[order], slot] = order.astype(np.int32)
+    token_rows = torch.from_numpy(tr_host).to(dev)
+    wt_host = np.where(tr_host >= 0, weight.cpu().numpy()[np.maximum(tr_host, 0)], 0.0)
+    token_weights = torch.from_numpy(wt_host.astype(np.float32)).to(dev)
+    combined = torch.empty((w.tokens, w.n), dtype=torch.bfloat16, device=dev)
+
+    def lib_combine(i):
+        moe_fp4.combine(prob.out, token_rows, token_weights, out=combined)
+
+    res = dict(fused_us=round(timed(fused), 2), zero_us=round(timed(zero), 2),
+               plain_gemm_us=round(timed(plain), 2), combine_us=round(timed(lib_combine), 2),
+               torch_index_add_us=round(timed(combine), 2))
+    comb_bytes = prob.m_total * w.n * 2 + w.tokens * w.n * 2 + w.tokens * topk * 8
+    res["combine_gbps"] = round(comb_bytes / (res["combine_us"] * 1e-6) / 1e9, 1)
+    # Parity of one fused call against the unfused pipeline on the same inputs (the
+    # oracle comparison is in the tests): both accumulate into zeroed buffers.
+    tokens.zero_()
+    fused(0)
+    got = tokens.clone()
+    tokens.zero_()
+    plain(0)
+    combine(0)
+    torch.cuda.synchronize()
+    err = ((got - tokens).norm(dim=1) / tokens.norm(dim=1).clamp_min(1e-30)).max().item()
+    res["max_token_rel_diff_fused_vs_torch"] = round(err, 6)
+    plain(0)
+    lib_combine(0)
+    torch.cuda.synchronize()
+    err2 = ((combined.float() - tokens).norm(dim=1) / tokens.norm(dim=1).clamp_min(1e-30)).max().item()
+    res["max_token_rel_diff_combine_vs_torch"] = round(err2, 6)
+    res["note"] = ("the two-pass and torch paths round rows to BF16 before summing, the fused "
+                   "path does not; the combine also rounds its output to BF16")
+    return res
+
+
 def plan_of(prob):
     from block_scaled_fp4_05_amd import moe_fp4
     w = prob.w
@@ -359,6 +454,11 @@ def main():
             "traffic": traffic, "algorithmic_bytes": int(prob.gemm_bytes),
             "avg_launch_us": round(r["gemm_ms"] * 1e3, 2)}
 
+    fin = None
+    if args.finalize:
+        fin = finalize_report(prob, args.steps)
+        log("finalize " + json.dumps(fin))
+
     secondary = None
     if args.secondary and args.secondary != "none" and args.secondary != args.workload:
         p2 = Problem(args.secondary, layout=args.layout)
@@ -400,6 +500,8 @@ def main():
         "parity_vs_oracle": par,
         "secondary": secondary,
     }
+    if fin is not None:
+        line["finalize"] = fin
     print(json.dumps(line), flush=True)
 
 

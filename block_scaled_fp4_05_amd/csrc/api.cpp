@@ -268,6 +268,44 @@ int moe_grouped_gemm_fp4_finalize(const uint8_t* a_q, const uint8_t* a_sf, const
                                row_weight, out, ldo, num_tokens, stream);
 }
 
+int moe_fp4_combine(const uint16_t* rows, int64_t ld_rows, int64_t m_total,
+                    const int32_t* token_rows, const float* token_weights, int32_t topk,
+                    int64_t num_tokens, int64_t n, const float* residual, int64_t ld_res,
+                    void* out, int out_dtype, int64_t ldo, void* stream) {
+  if (out_dtype != MOE_FP4_OUT_BF16 && out_dtype != MOE_FP4_OUT_FP32) return MOE_FP4_ERR_ARG;
+  if (!token_rows || !token_weights || !out || (m_total > 0 && !rows)) return MOE_FP4_ERR_NULL;
+  if (m_total < 0 || num_tokens < 0 || topk < 1 || n < 1 || ldo < n || (m_total > 0 && ld_rows < n) ||
+      (residual && ld_res < n))
+    return MOE_FP4_ERR_SHAPE;
+  const int64_t esize = out_dtype == MOE_FP4_OUT_FP32 ? 4 : 2;
+  if ((m_total > 0 && (!aligned(rows, 16) || ld_rows % 8 != 0)) || !aligned(out, 16) ||
+      (ldo * esize) % 16 != 0 || !aligned(token_rows, 4) || !aligned(token_weights, 4) ||
+      (residual && (!aligned(residual, 16) || ld_res % 4 != 0)))
+    return MOE_FP4_ERR_ALIGN;
+  if (n % 16 != 0) return MOE_FP4_ERR_UNSUPPORTED;
+  const int64_t lim = (int64_t)INT32_MAX - 4096;
+  if (m_total > lim / 2 / (ld_rows > 0 ? ld_rows : 1) || num_tokens > lim / esize / ldo ||
+      (residual && num_tokens > lim / 4 / ld_res) || num_tokens > lim / topk)
+    return MOE_FP4_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return MOE_FP4_OK;
+  moe_fp4::CombineArgs a;
+  a.rows = rows;
+  a.ld_rows = ld_rows;
+  a.m_total = m_total;
+  a.token_rows = token_rows;
+  a.token_weights = token_weights;
+  a.topk = topk;
+  a.num_tokens = num_tokens;
+  a.n = n;
+  a.residual = residual;
+  a.ld_res = ld_res;
+  a.out = out;
+  a.ldo = ldo;
+  a.f32_out = out_dtype == MOE_FP4_OUT_FP32 ? 1 : 0;
+  hipError_t err = moe_fp4::launch_combine(a, reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? MOE_FP4_OK : MOE_FP4_ERR_HIP;
+}
+
 int moe_fp4_pack_weights(const uint8_t* w_q, uint8_t* w_packed, int32_t num_experts,
                          int64_t n, int64_t k, void* stream) {
   return repack(w_q, w_packed, num_experts, n, k, stream, true);

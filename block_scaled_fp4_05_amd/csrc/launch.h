@@ -33,6 +33,24 @@ __host__ __device__ constexpr int32_t packed_granule(int64_t k) { return k % 512
 __host__ __device__ constexpr int32_t packed_block_bytes(int32_t granule) { return 8 * granule; }
 constexpr int kPackRows = 64;
 
+// Token-order combine of routed rows (combine.hip).
+struct CombineArgs {
+  const uint16_t* rows;  // BF16 [m_total][ld_rows]
+  int64_t ld_rows;
+  int64_t m_total;
+  const int32_t* token_rows;     // [num_tokens][topk], row index or < 0
+  const float* token_weights;    // [num_tokens][topk]
+  int32_t topk;
+  int64_t num_tokens;
+  int64_t n;
+  const float* residual;  // FP32 [num_tokens][ld_res] or NULL
+  int64_t ld_res;
+  void* out;              // BF16 or FP32 [num_tokens][ldo]
+  int64_t ldo;
+  int32_t f32_out;
+};
+hipError_t launch_combine(const CombineArgs& args, hipStream_t stream);
+
 // Rearrange weight codes between the row-major and the packed layout.
 hipError_t launch_repack(const uint8_t* src, uint8_t* dst, int32_t num_experts, int64_t n,
                          int64_t k, bool to_packed, hipStream_t stream);

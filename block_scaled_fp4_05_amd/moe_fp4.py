@@ -15,12 +15,13 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe_fp4.so")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_HIP, ERR_ARG = range(7)
+OUT_BF16, OUT_FP32 = 0, 1
 IN_BF16, IN_FP32 = 0, 1
 SCALE_STATIC, SCALE_DYNAMIC = 0, 1
 
 # Every symbol include/moe_fp4.h declares.
 EXPORTED = ("moe_fp4_quantize", "moe_grouped_gemm_fp4", "moe_grouped_gemm_fp4_packed",
-            "moe_grouped_gemm_fp4_finalize",
+            "moe_grouped_gemm_fp4_finalize", "moe_fp4_combine",
             "moe_fp4_pack_weights", "moe_fp4_unpack_weights", "moe_grouped_gemm_fp4_plan",
             "moe_fp4_stage_bytes", "moe_fp4_status_string", "moe_fp4_abi_version")
 
@@ -59,6 +60,8 @@ def lib() -> ctypes.CDLL:
     L.moe_grouped_gemm_fp4_finalize.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp, i, vp, i32, i64,
                                                  i64, i64, vp, vp, vp, i64, i64, vp]
     L.moe_grouped_gemm_fp4_finalize.restype = i
+    L.moe_fp4_combine.argtypes = [vp, i64, i64, vp, vp, i32, i64, i64, vp, i64, vp, i, i64, vp]
+    L.moe_fp4_combine.restype = i
     for f in (L.moe_fp4_pack_weights, L.moe_fp4_unpack_weights):
         f.argtypes = [vp, vp, i32, i64, i64, vp]
         f.restype = i
@@ -224,4 +227,29 @@ def grouped_gemm_finalize(a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets, out_t
         _ptr(row_weight), _ptr(out), out.stride(0), out.shape[0], _stream(stream))
     if st != OK:
         raise MoeFp4Error(st, "moe_grouped_gemm_fp4_finalize")
+    return out
+
+
+def combine_raw(*args):
+    """moe_fp4_combine with raw pointers (C argument order); returns the status."""
+    return lib().moe_fp4_combine(*args)
+
+
+def combine(rows, token_rows, token_weights, out=None, residual=None, out_dtype=torch.bfloat16,
+            stream=None):
+    """Token-order combine: out[t] = (residual[t] +) sum_s token_weights[t][s] * rows[token_rows[t][s]]
+    in FP32, slots in order.  rows: BF16 CUDA tensor [m_total][>= n] (the grouped GEMM's
+    output); token_rows int32 / token_weights float32 [num_tokens][topk].  Returns out
+    ([num_tokens][n] of out_dtype, bfloat16 or float32)."""
+    m_total, n = rows.shape
+    T, topk = token_rows.shape
+    if out is None:
+        out = torch.empty((T, n), dtype=out_dtype, device=rows.device)
+    dt = OUT_FP32 if out.dtype == torch.float32 else OUT_BF16
+    st = lib().moe_fp4_combine(_ptr(rows), rows.stride(0), m_total, _ptr(token_rows),
+                               _ptr(token_weights), topk, T, n, _ptr(residual),
+                               residual.stride(0) if residual is not None else 0, _ptr(out), dt,
+                               out.stride(0), _stream(stream))
+    if st != OK:
+        raise MoeFp4Error(st, "moe_fp4_combine")
     return out

@@ -249,6 +249,45 @@ int moe_grouped_gemm_fp4_finalize(const uint8_t* a_q, const uint8_t* a_sf, const
                                   const int32_t* out_token, const float* row_weight, float* out,
                                   int64_t ldo, int64_t num_tokens, void* stream);
 
+/* Output element types of moe_fp4_combine. */
+enum { MOE_FP4_OUT_BF16 = 0, MOE_FP4_OUT_FP32 = 1 };
+
+/*
+ * moe_fp4_combine -- the Mixture-of-Experts finalize step as a pass of its own:
+ * each token's output row is the routing-weighted sum of its top-k routed rows
+ * of the grouped GEMM's BF16 output (the final output write, "Peering into the
+ * CUTLASS Kernel", section "Input Knowledge Required", item 5, read as in
+ * moe_grouped_gemm_fp4_finalize).  For token t and column j < n:
+ *
+ *     acc = 0;  for s = 0 .. topk-1 with 0 <= r = token_rows[t][s] < m_total:
+ *                   acc = fl(acc + fl(token_weights[t][s] * rows[r][j]))
+ *     out[t][j] = round(residual ? fl(residual[t][j] + acc) : acc)
+ *
+ * in FP32, slots in order, rounded to BF16 (nearest even) or written as FP32.
+ * Deterministic: the same inputs give the same bits.  Unlike the finalize
+ * epilogue it needs the GEMM's per-row output, but it reads it with plain
+ * coalesced loads in one pass, where the epilogue adds every element with a
+ * device-wide atomic; on MI355X this pass plus the plain GEMM is the faster way.
+ *   rows          device, [m_total][ld_rows] BF16 (moe_grouped_gemm_fp4's out),
+ *                 16-byte aligned, ld_rows >= n and a multiple of 8.
+ *   token_rows    device, [num_tokens][topk] int32: the routed rows of each token,
+ *                 in summation order; an entry outside [0, m_total) is skipped.
+ *   token_weights device, [num_tokens][topk] float.
+ *   residual      device, [num_tokens][ld_res] FP32 added to the sum, or NULL;
+ *                 16-byte aligned, ld_res >= n and a multiple of 4.  out may be the
+ *                 same buffer (FP32 output, ldo == ld_res).
+ *   out           device, [num_tokens][ldo] of out_dtype, 16-byte aligned, ldo >= n,
+ *                 ldo a multiple of 8 (BF16) or 4 (FP32).  Columns >= n untouched.
+ *   n             a multiple of 16 (UNSUPPORTED otherwise).
+ * Errors: NULL, SHAPE (m_total < 0, num_tokens < 0, topk < 1, n < 1, ld_rows / ldo /
+ * ld_res < n), ALIGN, ARG (out_dtype), UNSUPPORTED (n % 16, any of the three
+ * buffers 2^31 - 4096 bytes or larger), HIP.  num_tokens == 0 is a no-op.
+ */
+int moe_fp4_combine(const uint16_t* rows, int64_t ld_rows, int64_t m_total,
+                    const int32_t* token_rows, const float* token_weights, int32_t topk,
+                    int64_t num_tokens, int64_t n, const float* residual, int64_t ld_res,
+                    void* out, int out_dtype, int64_t ldo, void* stream);
+
 /* Kernel configuration the GEMM picks for a problem (host-only, no GPU call). */
 typedef struct {
   int32_t tile_m;          /* rows of one expert per work item                       */

@@ -228,3 +228,30 @@ def test_finalize_rejects_tiles_it_does_not_run(tile, pk, monkeypatch):
     # epilogue; packed weights (512-element granule) need 512-element stages.
     monkeypatch.setenv("MOE_FP4_TILE", tile)
     assert _gf(k=1024, pk=pk) == 4
+
+
+def _cb(**kw):
+    a = dict(rows=P16, ld_rows=64, m=64, tok=P16, wt=P16, topk=2, T=32, n=64, res=None, ld_res=0,
+             out=P16, dt=0, ldo=64, stream=None)
+    a.update(kw)
+    return _lib().combine_raw(a["rows"], a["ld_rows"], a["m"], a["tok"], a["wt"], a["topk"], a["T"],
+                              a["n"], a["res"], a["ld_res"], a["out"], a["dt"], a["ldo"], a["stream"])
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=2), 6), (dict(rows=None), 1), (dict(tok=None), 1), (dict(wt=None), 1),
+    (dict(out=None), 1), (dict(topk=0), 2), (dict(T=-1), 2), (dict(n=0), 2), (dict(ldo=32), 2),
+    (dict(ld_rows=32), 2), (dict(res=P16, ld_res=32), 2), (dict(m=-1), 2),
+    (dict(rows=P16 + 8), 3), (dict(ld_rows=68), 3), (dict(out=P16 + 4), 3), (dict(ldo=68), 3),
+    (dict(dt=1, ldo=66), 3), (dict(tok=P16 + 2), 3), (dict(res=P16 + 8, ld_res=64), 3),
+    (dict(res=P16, ld_res=66), 3), (dict(n=24, ld_rows=32, ldo=32), 4),
+    (dict(T=1 << 26, ldo=64), 4),
+])
+def test_combine_rejects(kw, status):
+    assert _cb(**kw) == status
+
+
+@needs_no_gpu
+def test_combine_without_tokens_is_a_noop():
+    assert _cb(T=0) == 0
