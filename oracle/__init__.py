@@ -6,7 +6,10 @@ package.  The HIP library never does, and this package imports nothing from it.
 
   fp4_oracle.c   plain C99 + OpenMP: E2M1 / E4M3 codecs, the quantiser, the
                  grouped GEMM as an exact int64 sum and as an FP64 sum.
-  oracle.py      ctypes wrapper over the C oracle (numpy in, numpy out).
+  oracle.py      ctypes wrapper over the C oracle (numpy in, numpy out), and in
+                 plain numpy FP64 the steps around the GEMM: the token-order
+                 combine (finalize) and the SwiGLU activation of the gate+up
+                 projection.
   bruteforce.py  exact rational (Fractions) brute force for tiny shapes.
 
 Parity status: every function is pinned by the tests in ``tests/test_oracle_*``

@@ -279,3 +279,47 @@ def token_row_error(got: np.ndarray, ref: np.ndarray):
     safe = np.where(norm > 0, norm, 1.0)
     err = np.where(norm > 0, diff / safe, np.where(diff > 0, np.inf, 0.0))
     return err, norm
+
+
+# ------------------------------------------------- gate+up activation step --
+
+def silu(x: np.ndarray) -> np.ndarray:
+    """SiLU (the Swish gate of SwiGLU): x * sigmoid(x) = x / (1 + exp(-x)), in FP64.
+    Very negative x gives exp(-x) = inf and a result of -0.0, its limit."""
+    x = np.asarray(x, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return x / (1.0 + np.exp(-x))
+
+
+def swiglu(R: np.ndarray) -> np.ndarray:
+    """The gate+up activation of a Mixture-of-Experts FFN.
+
+    The pages allow the FINALIZE epilogue to apply an activation and a
+    quantisation to the GEMM result ("Peering into the CUTLASS Kernel", section
+    "Input Knowledge Required", item 5) without naming either.  Read here as the
+    gated-SiLU step between the two projections: the gate+up GEMM has n = 2I
+    output columns, the first I are the gate and the last I the up projection, and
+
+        h[r][i] = silu(R[r][i]) * R[r][I + i],   0 <= i < I.
+
+    R float64 [rows][2I] (the exact grouped-GEMM result, unrounded).  Evaluated in
+    FP64.  Returns float64 [rows][I]."""
+    R = np.asarray(R, dtype=np.float64)
+    if R.ndim != 2 or R.shape[1] % 2:
+        raise ValueError("swiglu: R must be [rows][2I]")
+    inter = R.shape[1] // 2
+    return silu(R[:, :inter]) * R[:, inter:]
+
+
+def swiglu_quantize(R: np.ndarray, g: float):
+    """The gate+up projection's output as the down projection reads it: the SwiGLU
+    activation of the exact GEMM result (swiglu), rounded once to FP32, then
+    NVFP4-quantised (quantize) with the static tensor scale g.  A single fused pass
+    cannot know the intermediate's amax before it has produced every row, so the
+    tensor scale is the caller's calibrated value.
+    Returns (h float64 [rows][I], q uint8 [rows][I/2], sf uint8 [rows][I/16])."""
+    h = swiglu(R)
+    if h.shape[1] % 16:
+        raise ValueError("swiglu_quantize: I must be a multiple of 16")
+    q, sf, _ = quantize(h.astype(np.float32), g=float(np.float32(g)))
+    return h, q, sf
