@@ -63,6 +63,9 @@ def parse_args():
     ap.add_argument("--layout", default="packed", choices=("packed", "rowmajor"),
                     help="weight-code layout the GEMM reads (default packed)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--swiglu", action="store_true",
+                    help="also time the gate+up GEMM with the SwiGLU + NVFP4 epilogue against "
+                         "the unfused GEMM, activation and quantiser")
     ap.add_argument("--finalize", action="store_true",
                     help="also time the finalize GEMM (routing-weighted sum into token order) "
                          "against the plain GEMM plus a separate weighted combine")
@@ -309,6 +312,79 @@ def finalize_report(prob, steps):
     return res
 
 
+def swiglu_report(prob, steps):
+    """The gate+up projection with the SwiGLU + NVFP4 epilogue on this workload (the
+    first half of the N weight rows is the gate, the second half the up projection;
+    weights N(0, 1/K), i.e. the workload's N(0,1) weights with their tensor scales
+    divided by sqrt(K), so the pre-activations are O(1) as in a trained layer), two ways:
+      fused    moe_grouped_gemm_fp4_swiglu: the NVFP4 intermediate straight from the GEMM;
+      unfused  the plain GEMM (BF16 rows), torch's silu(gate) * up in FP32, then
+               moe_fp4_quantize with the same static scale on the FP32 activation.
+    The static scale is the intermediate's amax / 2688 from one unfused pass (set-up)."""
+    import torch
+    from block_scaled_fp4_05_amd import moe_fp4
+    w = prob.w
+    if w.n % 32:
+        raise SystemExit("--swiglu needs N a multiple of 32 (N = 2I)")
+    inter = w.n // 2
+    dev = torch.device("cuda")
+    scaled = [(q, sf, (s / w.k ** 0.5).contiguous()) for q, sf, s in prob.weights]
+    h_scale = torch.empty(1, dtype=torch.float32, device=dev)
+    h_q = torch.empty((prob.m_total, inter // 2), dtype=torch.uint8, device=dev)
+    h_sf = torch.empty((prob.m_total, inter // 16), dtype=torch.uint8, device=dev)
+    u_q, u_sf = torch.empty_like(h_q), torch.empty_like(h_sf)
+
+    def timed(fn):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(steps):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps * 1e3
+
+    def fused(i):
+        w_q, w_sf, w_scale = scaled[i % len(scaled)]
+        moe_fp4.grouped_gemm_swiglu(prob.q, prob.sf, prob.g, w_q, w_sf, w_scale, prob.off, h_scale,
+                                    a_row_index=prob.idx, h_q=h_q, h_sf=h_sf,
+                                    m_total=prob.m_total, packed=prob.packed)
+
+    def plain(i):
+        w_q, w_sf, w_scale = scaled[i % len(scaled)]
+        moe_fp4.grouped_gemm(prob.q, prob.sf, prob.g, w_q, w_sf, w_scale, prob.off,
+                             a_row_index=prob.idx, out=prob.out, m_total=prob.m_total,
+                             packed=prob.packed)
+
+    def act():
+        y = prob.out.float()
+        return torch.nn.functional.silu(y[:, :inter]) * y[:, inter:]
+
+    def unfused(i):
+        plain(i)
+        moe_fp4.quantize(act(), tensor_scale=h_scale, q=u_q, sf=u_sf, dynamic=False)
+
+    plain(0)
+    h_scale.copy_(act().abs().max().reshape(1) / 2688.0)
+    res = dict(inter=inter, h_scale=round(h_scale.item(), 6), fused_us=round(timed(fused), 2),
+               unfused_us=round(timed(unfused), 2), plain_gemm_us=round(timed(plain), 2))
+    fused_bytes = (prob.gemm_bytes - prob.gemm_bytes_parts["output"]
+                   + prob.m_total * inter * (0.5 + 1.0 / 16.0) + 4.0)
+    res["fused_bytes"] = int(fused_bytes)
+    res["fused_gbps"] = round(fused_bytes / (res["fused_us"] * 1e-6) / 1e9, 1)
+    res["fused_hbm_frac"] = round(res["fused_gbps"] / HBM_PEAK_GBS, 4)
+    # Agreement of one fused call with the unfused pipeline (which rounds the GEMM
+    # output to BF16 before the activation); the oracle comparison is in the tests.
+    fused(0)
+    unfused(0)
+    torch.cuda.synchronize()
+    res["scale_mismatch_frac_vs_unfused"] = round((h_sf != u_sf).float().mean().item(), 5)
+    res["byte_mismatch_frac_vs_unfused"] = round((h_q != u_q).float().mean().item(), 5)
+    return res
+
+
 def plan_of(prob):
     from block_scaled_fp4_05_amd import moe_fp4
     w = prob.w
@@ -458,6 +534,9 @@ def main():
     if args.finalize:
         fin = finalize_report(prob, args.steps)
         log("finalize " + json.dumps(fin))
+    if args.swiglu:
+        swi = swiglu_report(prob, args.steps)
+        log("swiglu " + json.dumps(swi))
 
     secondary = None
     if args.secondary and args.secondary != "none" and args.secondary != args.workload:
@@ -502,6 +581,8 @@ def main():
     }
     if fin is not None:
         line["finalize"] = fin
+    if args.swiglu:
+        line["swiglu"] = swi
     print(json.dumps(line), flush=True)
 
 

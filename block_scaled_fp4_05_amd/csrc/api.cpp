@@ -217,6 +217,75 @@ int grouped_gemm_finalize(const uint8_t* a_q, const uint8_t* a_sf, const float* 
   return err == hipSuccess ? MOE_FP4_OK : MOE_FP4_ERR_HIP;
 }
 
+bool overlap(const void* p, int64_t pb, const void* q, int64_t qb) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  return pb > 0 && qb > 0 && a < b + (uintptr_t)qb && b < a + (uintptr_t)pb;
+}
+
+int grouped_gemm_swiglu(const uint8_t* a_q, const uint8_t* a_sf, const float* a_scale,
+                        int64_t a_rows, const int32_t* a_row_index, const uint8_t* w_q,
+                        const uint8_t* w_sf, const float* w_scale, int w_packed,
+                        const int32_t* expert_offsets, int32_t num_experts, int64_t m_total,
+                        int64_t n, int64_t k, const float* h_scale, uint8_t* h_q, uint8_t* h_sf,
+                        void* stream) {
+  if (!a_q || !a_sf || !a_scale || !w_q || !w_sf || !w_scale || !expert_offsets || !h_scale ||
+      !h_q || !h_sf)
+    return MOE_FP4_ERR_NULL;
+  if (w_packed != 0 && w_packed != 1) return MOE_FP4_ERR_ARG;
+  if (num_experts < 1 || m_total < 0 || n < 1 || k < 1 || a_rows < 0) return MOE_FP4_ERR_SHAPE;
+  if (!a_row_index && a_rows < m_total) return MOE_FP4_ERR_SHAPE;
+  if (m_total > 0 && a_rows < 1) return MOE_FP4_ERR_SHAPE;
+  const int s = check_gemm_shape(num_experts, m_total, n, k);
+  if (s != MOE_FP4_OK) return s;
+  if (!aligned(a_q, 16) || !aligned(a_sf, 16) || !aligned(w_q, 16) || !aligned(w_sf, 16) ||
+      !aligned(h_q, 16) || !aligned(h_sf, 16) || !aligned(a_scale, 4) || !aligned(w_scale, 4) ||
+      !aligned(h_scale, 4) || !aligned(expert_offsets, 4) ||
+      (a_row_index && !aligned(a_row_index, 4)))
+    return MOE_FP4_ERR_ALIGN;
+  if (a_rows * (k / 2) > (int64_t)INT32_MAX - 4096) return MOE_FP4_ERR_UNSUPPORTED;
+  // The intermediate has n/2 columns in whole 16-element blocks; packed weights
+  // are read in whole 64-row groups, which must not straddle the gate/up halves.
+  if (n % 32 != 0 || (w_packed && (n / 2) % 64 != 0)) return MOE_FP4_ERR_UNSUPPORTED;
+  // The outputs are written while the inputs are still being read.
+  const int64_t hq_bytes = m_total * (n / 4), hs_bytes = m_total * (n / 32);
+  if (overlap(h_q, hq_bytes, h_sf, hs_bytes) || overlap(h_q, hq_bytes, a_q, a_rows * (k / 2)) ||
+      overlap(h_q, hq_bytes, a_sf, a_rows * (k / 16)) ||
+      overlap(h_sf, hs_bytes, a_q, a_rows * (k / 2)) ||
+      overlap(h_sf, hs_bytes, a_sf, a_rows * (k / 16)))
+    return MOE_FP4_ERR_ARG;
+  GemmTile t = moe_fp4::choose_tile(num_experts, m_total, n, k, getenv("MOE_FP4_TILE"));
+  // Per-wave kernels with 4 row blocks (32 gate + 32 up rows) per item;
+  // experts large enough for the workgroup tile take four row blocks of rows.
+  if (t.tiled) t = GemmTile{4, 4, 4, k % 512 == 0 ? 2 : 1, k % 2048 == 0 ? 1 : 0, 0};
+  if (t.n_blocks != 4 || t.k_sub > 2) return MOE_FP4_ERR_UNSUPPORTED;
+  if (w_packed && t.k_sub != moe_fp4::packed_granule(k) / moe_fp4::kKStep)
+    return MOE_FP4_ERR_UNSUPPORTED;
+  if (m_total == 0) return MOE_FP4_OK;
+  GemmArgs p = {};
+  p.a_q = a_q;
+  p.a_sf = a_sf;
+  p.a_scale = a_scale;
+  p.a_row_index = a_row_index;
+  p.w_q = w_q;
+  p.w_sf = w_sf;
+  p.w_scale = w_scale;
+  p.offsets = expert_offsets;
+  p.a_rows = a_rows;
+  p.m_total = m_total;
+  p.n = n;
+  p.k = k;
+  p.ldo = n;
+  p.num_experts = num_experts;
+  p.n_tiles = (int32_t)((n / 2 + 31) / 32);
+  p.w_packed = w_packed;
+  p.h_q = h_q;
+  p.h_sf = h_sf;
+  p.h_scale = h_scale;
+  hipError_t err =
+      moe_fp4::launch_grouped_gemm_swiglu(p, t, reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? MOE_FP4_OK : MOE_FP4_ERR_HIP;
+}
+
 int repack(const uint8_t* src, uint8_t* dst, int32_t num_experts, int64_t n, int64_t k,
            void* stream, bool to_packed) {
   if (!src || !dst) return MOE_FP4_ERR_NULL;
@@ -266,6 +335,17 @@ int moe_grouped_gemm_fp4_finalize(const uint8_t* a_q, const uint8_t* a_sf, const
   return grouped_gemm_finalize(a_q, a_sf, a_scale, a_rows, a_row_index, w_q, w_sf, w_scale,
                                w_packed, expert_offsets, num_experts, m_total, n, k, out_token,
                                row_weight, out, ldo, num_tokens, stream);
+}
+
+int moe_grouped_gemm_fp4_swiglu(const uint8_t* a_q, const uint8_t* a_sf, const float* a_scale,
+                                int64_t a_rows, const int32_t* a_row_index,
+                                const uint8_t* w_q, const uint8_t* w_sf, const float* w_scale,
+                                int w_packed, const int32_t* expert_offsets, int32_t num_experts,
+                                int64_t m_total, int64_t n, int64_t k, const float* h_scale,
+                                uint8_t* h_q, uint8_t* h_sf, void* stream) {
+  return grouped_gemm_swiglu(a_q, a_sf, a_scale, a_rows, a_row_index, w_q, w_sf, w_scale,
+                             w_packed, expert_offsets, num_experts, m_total, n, k, h_scale, h_q,
+                             h_sf, stream);
 }
 
 int moe_fp4_combine(const uint16_t* rows, int64_t ld_rows, int64_t m_total,

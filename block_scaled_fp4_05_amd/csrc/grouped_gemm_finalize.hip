@@ -17,9 +17,9 @@ namespace {
 template <int KSUB, bool SL, bool PK>
 hipError_t launch_fin_mb(const GemmArgs& p, int m_blocks, hipStream_t stream) {
   switch (m_blocks) {
-    case 1: return launch_tile<1, 4, KSUB, 4, SL, PK, true>(p, stream);
-    case 2: return launch_tile<2, 4, KSUB, 4, SL, PK, true>(p, stream);
-    case 4: return launch_tile<4, 4, KSUB, 4, SL, PK, true>(p, stream);
+    case 1: return launch_tile<1, 4, KSUB, 4, SL, PK, kEpiFinalize>(p, stream);
+    case 2: return launch_tile<2, 4, KSUB, 4, SL, PK, kEpiFinalize>(p, stream);
+    case 4: return launch_tile<4, 4, KSUB, 4, SL, PK, kEpiFinalize>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1,6 +1,7 @@
 // The per-wavefront NVFP4 grouped-GEMM kernel template and its launcher, shared by
 // the translation units that instantiate it (grouped_gemm.hip: plain BF16 store;
-// grouped_gemm_finalize.hip: the routing-weighted token-order epilogue).
+// grouped_gemm_finalize.hip: the routing-weighted token-order epilogue;
+// grouped_gemm_swiglu.hip: the SwiGLU + NVFP4 epilogue of the gate+up projection).
 //
 // The problem: one GEMM per expert over the rows routed to it, all experts in
 // one launch ("Peering into the CUTLASS Kernel Cache", section "Knowledge
@@ -55,6 +56,30 @@ namespace {
 
 // K elements whose block scales fill one 128-byte line of a row.
 constexpr int kSpan = 2048;
+
+// What a finished item's epilogue does with its FP32 tile.
+enum Epilogue : int {
+  kEpiStore = 0,     // BF16 store of the routed rows (the plain GEMM)
+  kEpiFinalize = 1,  // routing-weighted FP32 adds into token rows
+  kEpiSwiglu = 2,    // SwiGLU of gate and up columns, NVFP4-quantised
+};
+
+// Weight rows of row block jb of an item at column n0.  With the SwiGLU
+// epilogue an item covers 32 columns of the intermediate: blocks 0 and 1 are
+// gate rows n0 .. n0+31, blocks 2 and 3 the matching up rows n/2 + n0 ..
+// (the first half of the weight rows is the gate, the second the up
+// projection); otherwise block jb is rows n0 + 16*jb ...
+template <bool SW>
+__device__ __forceinline__ int32_t block_row0(int32_t n0, int32_t n, int jb) {
+  if constexpr (SW) return (jb < 2 ? 0 : (n >> 1)) + n0 + 16 * (jb & 1);
+  else return n0 + 16 * jb;
+}
+// Whether row block jb holds weight rows (n % 16 == 0, so a block is all in or all out).
+template <bool SW>
+__device__ __forceinline__ bool block_in(int32_t n0, int32_t n, int jb) {
+  if constexpr (SW) return n0 + 16 * (jb & 1) < (n >> 1);
+  else return n0 + 16 * jb < n;
+}
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
@@ -144,7 +169,7 @@ __device__ __forceinline__ uint32_t mul24(int32_t a, int32_t b) {
   return __umul24((uint32_t)a, (uint32_t)b);
 }
 
-template <int MB, int NBW, int KSUB, bool PK>
+template <int MB, int NBW, int KSUB, bool PK, bool SW>
 __device__ __forceinline__ void item_loads(const ItemPos& it, const GemmArgs& p, int lane,
                                            const uint32_t (&rows)[MB], ItemLoads<MB, NBW>& ld) {
   const int c = lane & 15, g = lane >> 4;
@@ -153,17 +178,29 @@ __device__ __forceinline__ void item_loads(const ItemPos& it, const GemmArgs& p,
   ld.w = make_rsrc(p.w_q + (int64_t)it.e * n * kb, (uint32_t)(n * kb));
   ld.ws = make_rsrc(p.w_sf + (int64_t)it.e * n * nbk, (uint32_t)(n * nbk));
   ld.n0 = it.n0;
-  // Packed codes (PK, 64-column items): the item is one 64-row group; block
-  // jb of a stage holds rows 16*jb .. +15 in this kernel's lane order.
+  // Packed codes (PK, 64-column items): a row block of 16 rows starting at
+  // rb sits in the 64-row group rb / 64, at block (rb % 64) / 16 of each
+  // granule, in this kernel's lane order.  (For the plain mapping the item is
+  // one whole group; for SwiGLU every group is whole, n/2 % 64 == 0.)
   constexpr int32_t kBlock = 16 * 128 * KSUB;
 #pragma unroll
   for (int jb = 0; jb < NBW; ++jb) {
-    const int32_t row = it.n0 + 16 * jb + c;
-    const bool ok = row < n;
-    const uint32_t wv = PK ? (uint32_t)(it.n0 * kb + jb * kBlock + 16 * lane)
-                           : mul24(row, kb) + 32 * KSUB * g;
-    ld.w_voff[jb] = ok ? wv : kOutOfRange;
-    ld.ws_voff[jb] = ok ? mul24(row, nbk) + 4 * KSUB * g : kOutOfRange;
+    if constexpr (SW) {
+      const int32_t rb = block_row0<SW>(it.n0, n, jb);
+      const int32_t row = rb + c;
+      const bool ok = block_in<SW>(it.n0, n, jb);
+      const uint32_t wv = PK ? (uint32_t)((rb & ~63) * kb + ((rb & 63) >> 4) * kBlock + 16 * lane)
+                             : mul24(row, kb) + 32 * KSUB * g;
+      ld.w_voff[jb] = ok ? wv : kOutOfRange;
+      ld.ws_voff[jb] = ok ? mul24(row, nbk) + 4 * KSUB * g : kOutOfRange;
+    } else {
+      const int32_t row = it.n0 + 16 * jb + c;
+      const bool ok = row < n;
+      const uint32_t wv = PK ? (uint32_t)(it.n0 * kb + jb * kBlock + 16 * lane)
+                             : mul24(row, kb) + 32 * KSUB * g;
+      ld.w_voff[jb] = ok ? wv : kOutOfRange;
+      ld.ws_voff[jb] = ok ? mul24(row, nbk) + 4 * KSUB * g : kOutOfRange;
+    }
   }
   // Scale-line copies move 8 rows x 128 bytes per instruction: lane l takes
   // row l/8 and stores the row's 16-byte chunk (l%8) ^ (row%8) in LDS slot l%8,
@@ -217,7 +254,7 @@ struct LineCopy {
 // in-flight load still reads.  With SL, the stage first copies the 128-byte
 // scale lines of the item's 16*NBW weight rows for its span into LDS, or, if
 // it starts no span, issues the same copies out of range into the sink.
-template <int MB, int NBW, int KSUB, bool SL, bool PK>
+template <int MB, int NBW, int KSUB, bool SL, bool PK, bool SW>
 __device__ __forceinline__ void issue_loads(Stage<MB, NBW, KSUB>& st, const ItemLoads<MB, NBW>& it,
                                             const rsrc_t& a_rs, const rsrc_t& as_rs, int32_t kst,
                                             const LineCopy& lc, int32_t n, int32_t nbk) {
@@ -231,9 +268,11 @@ __device__ __forceinline__ void issue_loads(Stage<MB, NBW, KSUB>& st, const Item
     const int32_t soff = uniform(on ? lc.span * 128 : 0);
 #pragma unroll
     for (int i = 0; i < 2 * NBW; ++i) {
-      // Rows 8i .. 8i+7 of the tile: all inside n or all outside (n % 16 == 0).
-      const bool rows_ok = on && it.n0 + 8 * i < n;
-      const uint32_t voff = rows_ok ? it.sl_voff + (uint32_t)(8 * i * nbk) : kOutOfRange;
+      // Rows 8i .. 8i+7 of the tile (half i%2 of row block i/2): all inside n
+      // or all outside (n % 16 == 0).
+      const int32_t rows_at = SW ? block_row0<SW>(it.n0, n, i >> 1) + 8 * (i & 1) - it.n0 : 8 * i;
+      const bool rows_ok = on && (SW ? block_in<SW>(it.n0, n, i >> 1) : it.n0 + 8 * i < n);
+      const uint32_t voff = rows_ok ? it.sl_voff + (uint32_t)(rows_at * nbk) : kOutOfRange;
       uint8_t* dst = on ? lc.dst + 1024 * i : lc.dst;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(it.ws, (lds_ptr)dst, 16, voff, soff, 0, 0);
     }
@@ -403,9 +442,13 @@ struct PendingStores {
   uint32_t rvoff;
 };
 
-template <int MB, int NBW, bool STAGED>
+template <int MB, int NBW, bool STAGED, bool SW = false>
 __device__ __forceinline__ void hold_stores(const PendingStores<MB, NBW>& ps) {
-  if constexpr (STAGED) {
+  if constexpr (SW) {
+    // SwiGLU epilogue: per row block one code dword, one scale byte and their offsets.
+#pragma unroll
+    for (int ib = 0; ib < MB; ++ib) asm volatile("" ::"v"(ps.voff[ib]), "v"(ps.data[0][ib]), "v"(ps.data[1][ib]));
+  } else if constexpr (STAGED) {
     asm volatile("" ::"v"(ps.rvoff));
 #pragma unroll
     for (int k = 0; k < 2 * MB; ++k) asm volatile("" ::"v"(ps.rows[k]));
@@ -542,19 +585,110 @@ __device__ __forceinline__ void epilogue_finalize(float4_t (&acc)[NBW][MB], cons
   }
 }
 
+// SiLU in FP32: x / (1 + e^-x), with the device library's expf and an IEEE
+// division; very negative x gives e^-x = inf and the limit -0.
+__device__ __forceinline__ float silu_f32(float x) { return x / (1.0f + expf(-x)); }
+
+// SwiGLU + NVFP4 epilogue of the gate+up projection: the FINALIZE epilogue
+// with an activation and a quantisation ("Peering into the CUTLASS Kernel",
+// section "Input Knowledge Required", item 5), read as the gated SiLU between
+// the two projections of a Mixture-of-Experts FFN.  An item covers 32
+// intermediate columns i0 .. i0+31 (i0 = it.n0): acc[0..1] hold the gate
+// columns, acc[2..3] the up columns, so lane (c, g) holds, for row 16*ib + c,
+// elements 4g .. 4g+3 of intermediate blocks i0/16 (b = 0) and i0/16 + 1
+// (b = 1).  Per element, in FP32: gate and up = fl(acc * alpha) (the value the
+// plain path rounds to BF16), h = fl(silu(gate) * up).  Per 16-element block,
+// with the caller's static tensor scale gt: amax over the block (the 4 lanes
+// of a row exchange their maxima), scale = E4M3_RNE(fl(amax / fl(6 gt))),
+// s = fl(E4M3 value * gt), code = E2M1_RNE(fl(h / s)) (all zero when s = 0):
+// the activation quantiser's recipe with a static scale.  Output rows are the
+// routed rows (h_q [m_total][n/4], h_sf [m_total][n/32]), which the down
+// projection reads as its activations.  Lane g stores bytes 4g .. 4g+3 of the
+// row's 16 code bytes (gathered from two lanes) and lanes g = 0, 1 the scale
+// byte of block g; rows past the expert's end fall outside the item's store
+// resources and blocks past n/2 get an out-of-range offset.
+template <int MB, int NBW>
+__device__ __forceinline__ void epilogue_swiglu(float4_t (&acc)[NBW][MB], const ItemPos& it,
+                                                const GemmArgs& p, PendingStores<MB, NBW>& ps) {
+  static_assert(NBW == 4, "gate and up blocks of 32 intermediate columns");
+  // The lane number, read here rather than taken from the caller: the values
+  // derived from it below are then computed per epilogue instead of being
+  // hoisted out of the main loop, where they would hold registers (or spill)
+  // across every stage.
+  int lane;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+  const int c = lane & 15, g = lane >> 4;
+  const int32_t inter = (int32_t)(p.n >> 1);
+  const int32_t qrow = inter >> 1, srow = inter >> 4;  // bytes per row: codes, scales
+  const float gt = ((sconst_f32)p.h_scale)[0];
+  const float six_g = 6.0f * gt;
+  const rsrc_t oq = make_rsrc(p.h_q + (int64_t)it.row0 * qrow, (uint32_t)(it.rows_valid * qrow));
+  const rsrc_t os = make_rsrc(p.h_sf + (int64_t)it.row0 * srow, (uint32_t)(it.rows_valid * srow));
+  const bool q_ok = it.n0 + 16 * (g >> 1) < inter;
+  const bool s_ok = g < 2 && it.n0 + 16 * g < inter;
+  // Lane g's code bytes 4g .. 4g+3 are the 16-bit halves of lanes 2g and
+  // 2g+1 (mod 4) of the same row, for block g / 2.
+  const int src0 = c + 16 * ((2 * g) & 3), src1 = c + 16 * ((2 * g + 1) & 3);
+  const int sh = 16 * (g >> 1);
+#pragma unroll
+  for (int ib = 0; ib < MB; ++ib) {
+    uint32_t half[2], sfb[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const float4_t gv = acc[b][ib], uv = acc[2 + b][ib];
+      float h[4];
+      float m = 0.0f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float gate = gv[v] * it.alpha, up = uv[v] * it.alpha;
+        h[v] = silu_f32(gate) * up;
+        m = fmaxf(m, fabsf(h[v]));
+      }
+      m = fmaxf(m, __shfl_xor(m, 16, 64));
+      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      // E4M3 block scale, nearest even; clamping to 448 first makes it saturate.
+      const float r = fminf(m / six_g, 448.0f);
+      sfb[b] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(r, r, 0, false) & 0xFFu;
+      const float sc = __builtin_amdgcn_cvt_f32_fp8(sfb[b], 0) * gt;
+      const bool live = sc != 0.0f;
+      const float y0 = live ? h[0] / sc : 0.0f, y1 = live ? h[1] / sc : 0.0f;
+      const float y2 = live ? h[2] / sc : 0.0f, y3 = live ? h[3] / sc : 0.0f;
+      // E2M1 codes: nearest even, saturating, sign kept (element 2i low nibble).
+      const uint32_t c01 = (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y0, y1, 1.0f, 0) & 0xFFu;
+      const uint32_t c23 = (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y2, y3, 1.0f, 0) & 0xFFu;
+      half[b] = c01 | (c23 << 8);
+      acc[b][ib] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      acc[2 + b][ib] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    const uint32_t both = half[0] | (half[1] << 16);
+    const uint32_t v0 = (uint32_t)__shfl((int)both, src0, 64);
+    const uint32_t v1 = (uint32_t)__shfl((int)both, src1, 64);
+    const int32_t row = 16 * ib + c;
+    ps.data[0][ib][0] = ((v0 >> sh) & 0xFFFFu) | (((v1 >> sh) & 0xFFFFu) << 16);
+    ps.data[0][ib][1] = g == 0 ? sfb[0] : sfb[1];
+    ps.voff[ib] = q_ok ? (uint32_t)(row * qrow + (it.n0 >> 1) + 4 * g) : kOutOfRange;
+    ps.data[1][ib][0] = s_ok ? (uint32_t)(row * srow + (it.n0 >> 4) + g) : kOutOfRange;
+    __builtin_amdgcn_raw_buffer_store_b32(ps.data[0][ib][0], oq, ps.voff[ib], 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)ps.data[0][ib][1], os, ps.data[1][ib][0], 0, 0);
+  }
+}
+
 // Tiles of one or two row blocks with 256-element stages, and one-row-block
 // tiles with 512-element stages whose weight scales come through LDS, fit two
 // wavefronts per SIMD (at most 256 registers): ask for that, or the allocator
 // drifts past it and halves the wavefronts in flight.
-template <int MB, int NBW, int KSUB, int WAVES, bool SL, bool PK, int R, bool FIN>
+template <int MB, int NBW, int KSUB, int WAVES, bool SL, bool PK, int R, int EPI>
 __global__ __launch_bounds__(WAVES * 64)
 __attribute__((amdgpu_waves_per_eu((MB <= 2 && KSUB == 1) || (MB == 1 && KSUB == 2 && SL) ? 2 : 1)))
 void k_grouped_gemm(const GemmArgs p) {
   static_assert(R == 2 || (R == 3 && !SL), "a third register stage only without scale lines");
-  // Kernels without scale lines stage the epilogue through a per-wave LDS tile
-  // (the finalize epilogue adds in place and needs none).
-  constexpr bool STAGED = !SL && NBW == 4 && !FIN;
-  static_assert(!FIN || NBW == 4, "finalize kernels use 64-column items");
+  constexpr bool FIN = EPI == kEpiFinalize, SW = EPI == kEpiSwiglu;
+  // Kernels without scale lines stage the plain store through a per-wave LDS
+  // tile (the other epilogues need none).
+  constexpr bool STAGED = !SL && NBW == 4 && EPI == kEpiStore;
+  static_assert(EPI == kEpiStore || NBW == 4, "finalize and SwiGLU kernels use 4 row blocks");
+  // Output columns (intermediate columns with SwiGLU) per item.
+  constexpr int kItemCols = SW ? 32 : 16 * NBW;
   static_assert(!PK || NBW == 4, "packed weights are read by 64-column items");
   constexpr int BM = 16 * MB;
   constexpr int NTHR = WAVES * 64;
@@ -631,10 +765,10 @@ void k_grouped_gemm(const GemmArgs p) {
   // Row-index entries: of the item being started (first item), then of nx.
   const rsrc_t idx_rs = make_rsrc(p.a_row_index, p.a_row_index ? (uint32_t)(4 * m_total) : 0u);
   uint32_t nrow[MB];
-  ld_pos = locate(item_of(0), 0, wl, p, 16 * MB, 16 * NBW, lane);
+  ld_pos = locate(item_of(0), 0, wl, p, 16 * MB, kItemCols, lane);
 #pragma unroll
   for (int ib = 0; ib < MB; ++ib) nrow[ib] = row_index_load(idx_rs, ld_pos, ib, c);
-  item_loads<MB, NBW, KSUB, PK>(ld_pos, p, lane, nrow, l[0]);
+  item_loads<MB, NBW, KSUB, PK, SW>(ld_pos, p, lane, nrow, l[0]);
   // Finalize: each row's destination token and routing weight, fetched like
   // the row-index entries (ntok/nwt: of the item being started, then of nx)
   // and carried per register stage to the item's epilogue (ftok/fwt).
@@ -655,7 +789,7 @@ void k_grouped_gemm(const GemmArgs p) {
   // (the last item repeats itself; that copy is never used).
   auto locate_next = [&](int32_t round) {
     const int32_t r = round + 1 < my_items ? round + 1 : round;
-    nx = locate(item_of(r), ld_pos.e, wl, p, 16 * MB, 16 * NBW, lane);
+    nx = locate(item_of(r), ld_pos.e, wl, p, 16 * MB, kItemCols, lane);
   };
   locate_next(0);
   pos[0] = ld_pos;
@@ -681,7 +815,7 @@ void k_grouped_gemm(const GemmArgs p) {
       ld_st = 0;
       ++ld_round;
       ld_pos = nx;
-      item_loads<MB, NBW, KSUB, PK>(ld_pos, p, lane, nrow, dst);
+      item_loads<MB, NBW, KSUB, PK, SW>(ld_pos, p, lane, nrow, dst);
       locate_next(ld_round);
       return true;
     }
@@ -701,6 +835,7 @@ void k_grouped_gemm(const GemmArgs p) {
   auto retire = [&](const ItemPos& it, const int32_t (&tok)[MB], const float (&wt)[MB]) {
     if (++cp_st == nst) {
       if constexpr (FIN) epilogue_finalize<MB, NBW>(acc, it, c, g, p, tok, wt);
+      else if constexpr (SW) epilogue_swiglu<MB, NBW>(acc, it, p, ps);
       else if constexpr (STAGED) epilogue_staged<MB, NBW>(acc, it, lane, p, ps, out_tile);
       else epilogue<MB, NBW>(acc, it, c, g, p, ps);
       cp_st = 0;
@@ -740,14 +875,14 @@ void k_grouped_gemm(const GemmArgs p) {
       }
     }
     prefetch_rows();
-    issue_loads<MB, NBW, KSUB, SL, PK>(s[to], l[to], a_rs, as_rs, ld_st,
+    issue_loads<MB, NBW, KSUB, SL, PK, SW>(s[to], l[to], a_rs, as_rs, ld_st,
                                        more ? line_copy(ld_round, ld_st)
                                             : LineCopy{sl_base + 2 * kBufBytes, -1},
                                        n, nbk);
   };
 
   uint32_t wsd[NBW][KSUB];
-  issue_loads<MB, NBW, KSUB, SL, PK>(s[0], l[0], a_rs, as_rs, ld_st, line_copy(ld_round, ld_st), n, nbk);
+  issue_loads<MB, NBW, KSUB, SL, PK, SW>(s[0], l[0], a_rs, as_rs, ld_st, line_copy(ld_round, ld_st), n, nbk);
 #pragma unroll
   for (int r = 1; r < R - 1; ++r) issue(r, r - 1, r);
   bool done = false;
@@ -764,7 +899,7 @@ void k_grouped_gemm(const GemmArgs p) {
       stage_scales(s[r], wsd);
       compute_stage<MB, NBW, KSUB, SL>(s[r], wsd, pos[r].rows_valid, acc);
       hold<MB, NBW>(l[r]);
-      if constexpr (!SL) hold_stores<MB, NBW, STAGED>(ps);
+      if constexpr (!SL) hold_stores<MB, NBW, STAGED, SW>(ps);
       retire(pos[r], ftok[r], fwt[r]);
       done = u + r + 1 >= units;
     }
@@ -779,12 +914,12 @@ void k_grouped_gemm(const GemmArgs p) {
 template <int MB, int NBW, int KSUB, bool SL>
 constexpr int register_stages() { return 2; }
 
-template <int MB, int NBW, int KSUB, int WAVES, bool SL, bool PK = false, bool FIN = false>
+template <int MB, int NBW, int KSUB, int WAVES, bool SL, bool PK = false, int EPI = kEpiStore>
 hipError_t launch_tile(const GemmArgs& p, hipStream_t stream) {
-  auto kern = k_grouped_gemm<MB, NBW, KSUB, WAVES, SL, PK, register_stages<MB, NBW, KSUB, SL>(), FIN>;
+  auto kern = k_grouped_gemm<MB, NBW, KSUB, WAVES, SL, PK, register_stages<MB, NBW, KSUB, SL>(), EPI>;
   const size_t lds = worklist_bytes(p.num_experts) +
                      (SL ? (size_t)WAVES * scale_lds_per_wave<NBW>()
-                         : (NBW == 4 && !FIN ? (size_t)WAVES * out_tile_bytes<MB, NBW>() : 0));
+                         : (NBW == 4 && EPI == kEpiStore ? (size_t)WAVES * out_tile_bytes<MB, NBW>() : 0));
   int resident = 0;
   hipError_t err = resident_groups(kern, WAVES * 64, lds, &resident);
   if (err != hipSuccess) return err;

@@ -89,6 +89,11 @@ struct GemmArgs {
   float* fin_out;
   int64_t fin_ldo;
   int64_t num_tokens;
+  // SwiGLU epilogue only (moe_grouped_gemm_fp4_swiglu): the NVFP4 intermediate
+  // h_q [m_total][n/4], h_sf [m_total][n/32] at the static tensor scale *h_scale.
+  uint8_t* h_q;
+  uint8_t* h_sf;
+  const float* h_scale;
 };
 
 hipError_t launch_grouped_gemm(const GemmArgs& args, const GemmTile& tile, hipStream_t stream);
@@ -97,6 +102,11 @@ hipError_t launch_grouped_gemm(const GemmArgs& args, const GemmTile& tile, hipSt
 // kernels with 64-column items only.
 hipError_t launch_grouped_gemm_finalize(const GemmArgs& args, const GemmTile& tile,
                                         hipStream_t stream);
+
+// The same GEMM with the SwiGLU + NVFP4 epilogue (grouped_gemm_swiglu.hip):
+// per-wave kernels, items of 32 intermediate columns (4 row blocks).
+hipError_t launch_grouped_gemm_swiglu(const GemmArgs& args, const GemmTile& tile,
+                                      hipStream_t stream);
 
 // Workgroup-tiled kernel (grouped_gemm_tiled.hip): 128 x 128 items, 4 waves.
 hipError_t launch_grouped_gemm_tiled(const GemmArgs& args, hipStream_t stream);

@@ -21,7 +21,7 @@ SCALE_STATIC, SCALE_DYNAMIC = 0, 1
 
 # Every symbol include/moe_fp4.h declares.
 EXPORTED = ("moe_fp4_quantize", "moe_grouped_gemm_fp4", "moe_grouped_gemm_fp4_packed",
-            "moe_grouped_gemm_fp4_finalize", "moe_fp4_combine",
+            "moe_grouped_gemm_fp4_finalize", "moe_grouped_gemm_fp4_swiglu", "moe_fp4_combine",
             "moe_fp4_pack_weights", "moe_fp4_unpack_weights", "moe_grouped_gemm_fp4_plan",
             "moe_fp4_stage_bytes", "moe_fp4_status_string", "moe_fp4_abi_version")
 
@@ -60,6 +60,9 @@ def lib() -> ctypes.CDLL:
     L.moe_grouped_gemm_fp4_finalize.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp, i, vp, i32, i64,
                                                  i64, i64, vp, vp, vp, i64, i64, vp]
     L.moe_grouped_gemm_fp4_finalize.restype = i
+    L.moe_grouped_gemm_fp4_swiglu.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp, i, vp, i32, i64,
+                                               i64, i64, vp, vp, vp, vp]
+    L.moe_grouped_gemm_fp4_swiglu.restype = i
     L.moe_fp4_combine.argtypes = [vp, i64, i64, vp, vp, i32, i64, i64, vp, i64, vp, i, i64, vp]
     L.moe_fp4_combine.restype = i
     for f in (L.moe_fp4_pack_weights, L.moe_fp4_unpack_weights):
@@ -228,6 +231,38 @@ def grouped_gemm_finalize(a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets, out_t
     if st != OK:
         raise MoeFp4Error(st, "moe_grouped_gemm_fp4_finalize")
     return out
+
+
+def swiglu_raw(*args):
+    """moe_grouped_gemm_fp4_swiglu with raw pointers (C argument order); returns the status."""
+    return lib().moe_grouped_gemm_fp4_swiglu(*args)
+
+
+def grouped_gemm_swiglu(a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets, h_scale,
+                        a_row_index=None, h_q=None, h_sf=None, m_total: int | None = None,
+                        packed: bool = False, stream=None):
+    """Gate+up grouped GEMM with the SwiGLU + NVFP4 epilogue.  w_q [E][2I][k/2]: rows
+    0..I-1 the gate, I..2I-1 the up projection; h_scale float32 CUDA tensor [1], the
+    intermediate's static tensor scale.  Other arguments as grouped_gemm.  Returns
+    (h_q uint8 [m_total][I/2], h_sf uint8 [m_total][I/16]), the down projection's
+    activations (or the given buffers)."""
+    E, n, kb = w_q.shape
+    k = 2 * kb
+    a_rows = a_q.shape[0]
+    if m_total is None:
+        m_total = a_row_index.shape[0] if a_row_index is not None else a_rows
+    dev = w_q.device
+    if h_q is None:
+        h_q = torch.empty((m_total, n // 4), dtype=torch.uint8, device=dev)
+    if h_sf is None:
+        h_sf = torch.empty((m_total, n // 32), dtype=torch.uint8, device=dev)
+    st = lib().moe_grouped_gemm_fp4_swiglu(
+        _ptr(a_q), _ptr(a_sf), _ptr(a_scale), a_rows, _ptr(a_row_index), _ptr(w_q), _ptr(w_sf),
+        _ptr(w_scale), 1 if packed else 0, _ptr(offsets), E, m_total, n, k, _ptr(h_scale),
+        _ptr(h_q), _ptr(h_sf), _stream(stream))
+    if st != OK:
+        raise MoeFp4Error(st, "moe_grouped_gemm_fp4_swiglu")
+    return h_q, h_sf
 
 
 def combine_raw(*args):

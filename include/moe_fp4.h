@@ -249,6 +249,56 @@ int moe_grouped_gemm_fp4_finalize(const uint8_t* a_q, const uint8_t* a_sf, const
                                   const int32_t* out_token, const float* row_weight, float* out,
                                   int64_t ldo, int64_t num_tokens, void* stream);
 
+/*
+ * moe_grouped_gemm_fp4_swiglu -- the gate+up projection of a Mixture-of-Experts
+ * FFN with the activation and the down projection's input quantisation in its
+ * epilogue: the grouped GEMM's result is never written; each routed row leaves
+ * as the NVFP4 encoding of its SwiGLU activation, ready to be the activations
+ * (a_q, a_sf, a_scale = h_scale) of the down projection's grouped GEMM.  The
+ * pages allow the final-write epilogue to apply an activation and a
+ * quantisation ("Peering into the CUTLASS Kernel", section "Input Knowledge
+ * Required", item 5); this library reads that as the gated SiLU between the two
+ * projections, followed by this library's NVFP4 recipe at a static scale.
+ *
+ * The weights have n = 2I rows per expert: rows 0 .. I-1 are the gate, rows
+ * I .. 2I-1 the up projection.  For routed row r of expert e and i < I, in FP32:
+ *
+ *     gate = fl(acc(r, i) * alpha),  up = fl(acc(r, I + i) * alpha)
+ *     h    = fl(silu(gate) * up),    silu(x) = x / (1 + e^-x)
+ *
+ * with acc and alpha = fl(a_scale * w_scale[e]) as in moe_grouped_gemm_fp4 (the
+ * value the plain GEMM rounds to BF16), e^-x from the device math library.  Then,
+ * per row and block of 16 consecutive intermediate columns, with g = *h_scale:
+ *
+ *     sf = E4M3_RNE(fl(amax |h| / fl(6 g))),  s = fl(E4M3(sf) * g),
+ *     code = E2M1_RNE(fl(h / s))  (0 when s = 0)
+ *
+ * exactly the steps of moe_fp4_quantize in MOE_FP4_SCALE_STATIC mode.  A single
+ * pass cannot know the intermediate's amax before every row is done, so the
+ * tensor scale is static: a calibrated value the caller supplies.
+ * Arguments as moe_grouped_gemm_fp4_finalize for the GEMM (w_packed: 0 =
+ * row-major w_q, 1 = the packed layout), plus:
+ *   n        2I, a multiple of 32; with w_packed, I a multiple of 64.
+ *   h_scale  device, 1 float: g, positive and finite (not checked).
+ *   h_q      device, [m_total][n/4] bytes (I/2 per row, two codes a byte, element
+ *            2i in the low nibble), 16-byte aligned; written for every routed row.
+ *   h_sf     device, [m_total][n/32] E4M3 block scales, 16-byte aligned.
+ * Rows follow the routed order (row r of expert e's range), like out of
+ * moe_grouped_gemm_fp4.  Deterministic.  The kernel runs per-wavefront items
+ * of 32 intermediate columns (experts of any size).
+ * Errors: as moe_grouped_gemm_fp4, plus NULL (h_scale, h_q, h_sf), ALIGN (h_q,
+ * h_sf not 16-byte aligned; h_scale not 4-byte aligned), ARG (w_packed not 0 or
+ * 1; h_q, h_sf, a_q, a_sf overlapping), UNSUPPORTED (n % 32, or I % 64 with
+ * packed weights, or a MOE_FP4_TILE override this epilogue does not run).
+ * m_total == 0 is a no-op.
+ */
+int moe_grouped_gemm_fp4_swiglu(const uint8_t* a_q, const uint8_t* a_sf, const float* a_scale,
+                                int64_t a_rows, const int32_t* a_row_index,
+                                const uint8_t* w_q, const uint8_t* w_sf, const float* w_scale,
+                                int w_packed, const int32_t* expert_offsets, int32_t num_experts,
+                                int64_t m_total, int64_t n, int64_t k, const float* h_scale,
+                                uint8_t* h_q, uint8_t* h_sf, void* stream);
+
 /* Output element types of moe_fp4_combine. */
 enum { MOE_FP4_OUT_BF16 = 0, MOE_FP4_OUT_FP32 = 1 };
 

@@ -230,6 +230,44 @@ def test_finalize_rejects_tiles_it_does_not_run(tile, pk, monkeypatch):
     assert _gf(k=1024, pk=pk) == 4
 
 
+H_Q, H_SF = 0x4000000, 0x8000000  # fake output addresses clear of the inputs at P16
+
+
+def _gs(**kw):
+    a = dict(a_q=P16, a_sf=P16, a_scale=P16, a_rows=64, idx=None, w_q=P16, w_sf=P16, w_scale=P16,
+             pk=0, off=P16, E=4, m=64, n=128, k=512, hs=P16, hq=H_Q, hsf=H_SF, stream=None)
+    a.update(kw)
+    return _lib().swiglu_raw(a["a_q"], a["a_sf"], a["a_scale"], a["a_rows"], a["idx"], a["w_q"],
+                             a["w_sf"], a["w_scale"], a["pk"], a["off"], a["E"], a["m"], a["n"],
+                             a["k"], a["hs"], a["hq"], a["hsf"], a["stream"])
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("kw,status", [
+    (dict(hs=None), 1), (dict(hq=None), 1), (dict(hsf=None), 1), (dict(w_q=None), 1),
+    (dict(off=None), 1), (dict(pk=2), 6), (dict(E=0), 2), (dict(m=-1), 2), (dict(a_rows=32), 2),
+    (dict(n=48), 4), (dict(n=16), 4), (dict(pk=1, n=64), 4), (dict(pk=1, n=160), 4), (dict(k=320), 4),
+    (dict(hq=H_Q + 4), 3), (dict(hsf=H_SF + 2), 3), (dict(hs=P16 + 2), 3), (dict(a_q=P16 + 8), 3),
+    (dict(hq=P16), 6), (dict(hsf=P16 + 64), 6), (dict(hsf=H_Q + 512), 6),
+])
+def test_swiglu_rejects(kw, status):
+    assert _gs(**kw) == status
+
+
+@needs_no_gpu
+def test_swiglu_empty_problem_is_a_noop():
+    assert _gs(m=0, a_rows=0) == 0
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("tile,pk", [("16x32", 0), ("32x32x1024", 0), ("16x64x256", 1)])
+def test_swiglu_rejects_tiles_it_does_not_run(tile, pk, monkeypatch):
+    # As for the finalize epilogue: 4 row blocks per item, stages of 256 or 512
+    # elements, and packed weights need their granule as the stage.
+    monkeypatch.setenv("MOE_FP4_TILE", tile)
+    assert _gs(k=1024, pk=pk) == 4
+
+
 def _cb(**kw):
     a = dict(rows=P16, ld_rows=64, m=64, tok=P16, wt=P16, topk=2, T=32, n=64, res=None, ld_res=0,
              out=P16, dt=0, ldo=64, stream=None)

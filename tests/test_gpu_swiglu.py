@@ -1,0 +1,244 @@
+"""GPU parity of the gate+up grouped GEMM with the SwiGLU + NVFP4 epilogue
+(moe_grouped_gemm_fp4_swiglu) against the oracle: the exact GEMM result (oracle
+grouped_gemm), its SwiGLU in FP64 (oracle swiglu) and the NVFP4 encoding at the
+static tensor scale (oracle swiglu_quantize).
+
+The kernel takes every encoding decision in FP32 on its own FP32 accumulation,
+the oracle on the exact value, so a value within rounding distance of a decision
+boundary may legitimately encode either way.  The check is therefore two-fold:
+
+* validity, for every block and element: with tau an upper bound on the distance
+  between the kernel's FP32 h and the exact h (from the FP32 accumulation bound
+  K * 2^-24 * sum |a * w| of the GEMM, carried through SwiGLU, plus the
+  rounding of the FP32 activation), the kernel's block scale is one that some
+  block amax within tau of the exact one gives, and each element code (under the
+  kernel's own block scale) one that some value within tau of the exact h gives;
+* agreement: the kernel's scales and codes equal the oracle's nominal encoding
+  except for at most 0.1% of blocks and elements (the ones near a boundary).
+
+Rows past m_total (guard rows) must stay untouched."""
+import numpy as np
+import pytest
+import torch
+
+import wl_data
+from gpu_util import dev, require_gpu, say
+from oracle import oracle as orc
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -24  # FP32 unit round-off
+GUARD = 0xA5
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _problem(T, E, topk, inter, k, seed, gather=True, target_std=2.0, exact=False):
+    """T tokens routed to topk distinct experts each; rows sorted by (expert, token).
+    The expert scales put the gate/up pre-activations at about target_std, so the
+    SiLU works in its curved range.
+
+    exact: block scales drawn from {0.5, 1, 2} and tensor scales powers of two, so
+    every product of dequantised values is a multiple of 1/16 below 144 in
+    magnitude and every partial sum (far below 2^20) is exact in FP32 in any
+    order: the kernel's gate and up values are then the exact ones, and only the
+    FP32 SiLU and product separate its h from the oracle's."""
+    rng = np.random.default_rng(seed)
+    n = 2 * inter
+    pairs = sorted((int(e), t) for t in range(T) for e in rng.choice(E, topk, replace=False))
+    row_token = np.array([t for _, t in pairs], np.int32)
+    counts = np.bincount([e for e, _ in pairs], minlength=E)
+    off = np.zeros(E + 1, np.int32)
+    off[1:] = np.cumsum(counts)
+    m = int(off[-1])
+    a_q = gen.random_fp4_bytes((T, k // 2), seed + 1)
+    a_sf = gen.random_e4m3_codes((T, k // 16), seed + 2, 0x30, 0x40)
+    w_sf = gen.random_e4m3_codes((E, n, k // 16), seed + 4, 0x30, 0x40)
+    if exact:  # 0x30, 0x38, 0x40 are 0.5, 1 and 2
+        a_sf = (0x30 + 8 * (a_sf % 3)).astype(np.uint8)
+        w_sf = (0x30 + 8 * (w_sf % 3)).astype(np.uint8)
+    if not gather:  # activations already in routed order, one row per routed row
+        a_q, a_sf = a_q[row_token], a_sf[row_token]
+    # Random E2M1 codes have mean square 12.6 and the E4M3 scales 0x30..0x40
+    # (0.5..2) about 1.4: an unscaled dot product of k terms has std ~ 18 sqrt(k).
+    base = target_std / (18.0 * np.sqrt(k))
+    w_scale = base * rng.uniform(0.5, 2.0, E)
+    if exact:
+        w_scale = 2.0 ** np.round(np.log2(w_scale))
+    return dict(
+        a_q=a_q, a_sf=a_sf, a_scale=np.float32(1.0),
+        w_q=gen.random_fp4_bytes((E, n, k // 2), seed + 3), w_sf=w_sf,
+        w_scale=w_scale.astype(np.float32),
+        offsets=off, m_total=m, row_index=row_token if gather else None, exact=exact)
+
+
+def _gpu_swiglu(P, g2, packed=False, guard_rows=3):
+    from block_scaled_fp4_05_amd import moe_fp4
+    m, n = P["m_total"], P["w_q"].shape[1]
+    hq = torch.full((m + guard_rows, n // 4), GUARD, dtype=torch.uint8, device="cuda")
+    hs = torch.full((m + guard_rows, n // 32), GUARD, dtype=torch.uint8, device="cuda")
+    w_q = dev(P["w_q"])
+    if packed:
+        w_q = moe_fp4.pack_weights(w_q)
+    idx = P["row_index"]
+    moe_fp4.grouped_gemm_swiglu(
+        dev(P["a_q"]), dev(P["a_sf"]), dev(np.array([P["a_scale"]], np.float32)), w_q,
+        dev(P["w_sf"]), dev(P["w_scale"]), dev(P["offsets"]), dev(np.array([g2], np.float32)),
+        a_row_index=None if idx is None else dev(idx), h_q=hq, h_sf=hs, m_total=m, packed=packed)
+    torch.cuda.synchronize()
+    q, s = hq.cpu().numpy(), hs.cpu().numpy()
+    assert np.all(q[m:] == GUARD) and np.all(s[m:] == GUARD), "rows past m_total were written"
+    return q[:m], s[:m]
+
+
+def _oracle_parts(P, rows_sel=None):
+    """Exact GEMM result R and the bound S = sum |a * w| * alpha per element."""
+    args = (P["a_q"], P["a_sf"], P["a_scale"], P["w_q"], P["w_sf"], P["w_scale"], P["offsets"])
+    R, _ = orc.grouped_gemm(*args, a_row_index=P["row_index"], rows_sel=rows_sel)
+    # |a * w| summed: clear the sign bit of every code (bit 3 of each nibble).
+    S = orc.grouped_gemm_f64(P["a_q"] & 0x77, P["a_sf"], abs(P["a_scale"]), P["w_q"] & 0x77,
+                             P["w_sf"], np.abs(P["w_scale"]), P["offsets"],
+                             a_row_index=P["row_index"], rows_sel=rows_sel)
+    return R, S
+
+
+def _nibbles(q):
+    return np.stack([q & 0xF, q >> 4], axis=-1).reshape(q.shape[0], -1)
+
+
+def _e2m1_value(codes):
+    mag = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])[codes & 7]
+    return np.where(codes & 8, -mag, mag)
+
+
+def _check(q, sf, R, S, g2, k, label, exact=False):
+    inter = R.shape[1] // 2
+    h, q_ref, sf_ref = orc.swiglu_quantize(R, g2)
+    # Distance bound between the kernel's FP32 gate / up values and the exact
+    # ones: the FP32 accumulation bound, or none when the sums are exact.
+    e = (np.zeros_like(R) if exact else 2.0 * k * U * S + 2.0 * U * np.abs(R)) + 1e-37
+    gate, up = R[:, :inter], R[:, inter:]
+    e_g, e_u = e[:, :inter], e[:, inter:]
+    tau = 1.1 * e_g * (np.abs(up) + e_u) + np.abs(orc.silu(gate)) * e_u + 2.0 ** -20 * np.abs(h) + 1e-37
+    rows, nb = sf.shape
+    g32 = np.float32(g2)
+    six_g = np.float32(6.0) * g32
+    hb, tb = h.reshape(rows, nb, 16), tau.reshape(rows, nb, 16)
+    # Block scales: any amax within tau, through fl(amax / fl(6 g)) and the encoder.
+    a_lo = np.nextafter(np.max(np.maximum(np.abs(hb) - tb, 0.0), axis=2).astype(np.float32), np.float32(0))
+    a_hi = np.nextafter(np.max(np.abs(hb) + tb, axis=2).astype(np.float32), np.float32(np.inf))
+    s_lo = orc.e4m3_encode_array(np.minimum(a_lo / six_g, np.float32(448)))
+    s_hi = orc.e4m3_encode_array(np.minimum(a_hi / six_g, np.float32(448)))
+    bad = (sf < s_lo) | (sf > s_hi)
+    assert not np.any(bad), f"{label}: block scale outside what the exact amax allows at {np.argwhere(bad)[:3]}"
+    # Element codes under the kernel's own scale.
+    dec = np.array([orc.e4m3_decode(int(c)) for c in range(256)], np.float64)
+    s = (dec[sf].astype(np.float32) * g32)[:, :, None]
+    codes = _nibbles(q).reshape(rows, nb, 16)
+    live = np.broadcast_to(s != 0, codes.shape)
+    assert np.all(codes[~live] == 0), f"{label}: nonzero code in a block with scale 0"
+    with np.errstate(divide="ignore", invalid="ignore"):
+        lo = np.nextafter((hb - tb).astype(np.float32), np.float32(-np.inf)) / s
+        hi = np.nextafter((hb + tb).astype(np.float32), np.float32(np.inf)) / s
+    lo, hi = np.where(live, lo, 0), np.where(live, hi, 0)
+    v = _e2m1_value(codes)
+    v_lo = _e2m1_value(orc.e2m1_encode_array(lo.astype(np.float32)))
+    v_hi = _e2m1_value(orc.e2m1_encode_array(hi.astype(np.float32)))
+    ok = (v >= v_lo) & (v <= v_hi)
+    ok &= ~((hi < 0) & ((codes & 8) == 0)) & ~((lo > 0) & ((codes & 8) != 0))  # sign of +-0
+    ok |= ~live
+    assert np.all(ok), f"{label}: element code outside what the exact value allows at {np.argwhere(~ok)[:3]}"
+    # Agreement with the nominal encoding.
+    same_sf = sf == sf_ref
+    codes_ref = _nibbles(q_ref).reshape(rows, nb, 16)
+    diff_codes = int(np.sum((codes != codes_ref) & same_sf[:, :, None]))
+    n_sf, n_el = sf.size, codes.size
+    lim_sf, lim_el = (2, 2) if exact else (max(2, n_sf // 1000), max(2, n_el // 1000))
+    assert n_sf - int(same_sf.sum()) <= lim_sf, f"{label}: {n_sf - same_sf.sum()} scale mismatches"
+    assert diff_codes <= lim_el, f"{label}: {diff_codes} code mismatches"
+    return n_sf - int(same_sf.sum()), diff_codes
+
+
+def _calibrated(R):
+    """The static scale a calibration pass would pick: amax of the FP32 activation / 2688."""
+    return float(np.float32(np.float32(np.max(np.abs(orc.swiglu(R).astype(np.float32)))) / np.float32(2688)))
+
+
+# (T, E, topk, I, k): average rows per expert 8 / 24 / 32 / 66 / 150 (one, two and
+# four row blocks, and experts the plain GEMM would give the workgroup tile), 256-
+# and 512-element stages, LDS scale lines (k % 2048 == 0), intermediates whose last
+# item holds one 16-column block (I % 32 == 16), and many empty experts.
+CASES = [(32, 8, 2, 64, 256), (48, 6, 3, 80, 512), (64, 4, 2, 128, 2048), (100, 3, 2, 64, 768),
+         (300, 2, 1, 64, 512), (40, 5, 4, 112, 6144), (6, 40, 2, 128, 512)]
+
+
+@pytest.mark.parametrize("exact", [True, False])
+@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_swiglu_matches_oracle(case, packed, exact):
+    T, E, topk, inter, k = CASES[case]
+    if packed and inter % 64:
+        pytest.skip("packed weights need I % 64 == 0")
+    P = _problem(T, E, topk, inter, k, 900 + 10 * case, exact=exact)
+    R, S = _oracle_parts(P)
+    g2 = _calibrated(R)
+    say(f"swiglu T={T} E={E} top{topk} I={inter} k={k} packed={packed} exact={exact} g={g2:.4g}")
+    q, sf = _gpu_swiglu(P, g2, packed=packed)
+    _check(q, sf, R, S, g2, k, f"case {case}", exact=exact)
+
+
+@pytest.mark.parametrize("factor", [1.0 / 16, 8.0])
+def test_swiglu_static_scale_saturating_and_coarse(factor):
+    # 1/16 of the calibrated scale: many blocks saturate (scale 448, codes +-6);
+    # 8x: block scales in the E4M3 subnormal range.
+    P = _problem(64, 4, 2, 128, 512, 977, exact=True)
+    R, S = _oracle_parts(P)
+    g2 = _calibrated(R) * factor
+    say(f"swiglu static scale x{factor}")
+    q, sf = _gpu_swiglu(P, g2)
+    _check(q, sf, R, S, g2, 512, f"scale x{factor}", exact=True)
+    if factor < 1:
+        assert np.any(sf == 0x7E)
+
+
+def test_swiglu_without_row_index():
+    P = _problem(40, 6, 2, 64, 512, 981, gather=False, exact=True)
+    R, S = _oracle_parts(P)
+    g2 = _calibrated(R)
+    say("swiglu without row index")
+    q, sf = _gpu_swiglu(P, g2)
+    _check(q, sf, R, S, g2, 512, "no row index", exact=True)
+
+
+def test_swiglu_is_deterministic_and_packed_equals_rowmajor():
+    P = _problem(48, 8, 2, 128, 2048, 985)
+    R, _ = _oracle_parts(P)
+    g2 = _calibrated(R)
+    say("swiglu repeatability")
+    a = _gpu_swiglu(P, g2)
+    b = _gpu_swiglu(P, g2)
+    c = _gpu_swiglu(P, g2, packed=True)
+    for x, y in ((a, b), (a, c)):
+        assert np.array_equal(x[0], y[0]) and np.array_equal(x[1], y[1])
+
+
+def test_swiglu_full_size_gate_up_shard():
+    """The decode gate+up shard at full size (256 experts x 16 rows, K = 6144,
+    N = 2I = 512), packed weights, in the launch configuration the bench times;
+    sampled rows against the oracle.  Weights N(0, 1/K) (the N(0,1) workload
+    weights with their tensor scales divided by sqrt(K)), so pre-activations are O(1)."""
+    d = wl_data.workload("c3")
+    k = d["w"].k
+    P = dict(a_q=d["a_q"], a_sf=d["a_sf"], a_scale=d["a_scale"], w_q=d["w_q"], w_sf=d["w_sf"],
+             w_scale=(d["w_scale"] / np.float32(np.sqrt(k))).astype(np.float32),
+             offsets=d["offsets"], m_total=d["m_total"], row_index=d["row_token"])
+    sel = wl_data.sample_rows(P["offsets"], 96, 41)
+    R, S = _oracle_parts(P, rows_sel=sel)
+    g2 = _calibrated(R)
+    say(f"swiglu full gate+up shard m_total={P['m_total']} (sampled rows), g={g2:.4g}")
+    q, sf = _gpu_swiglu(P, g2, packed=True)
+    _check(q[sel], sf[sel], R, S, g2, k, "c3 swiglu")
