@@ -171,6 +171,21 @@ class Problem:
                              packed=self.packed)
 
 
+def warm(fn, seconds=0.25, min_calls=3):
+    """Run fn back to back for about `seconds` (at least min_calls), then synchronise:
+    long enough for the GPU's clocks to settle under the kernel's own load, which a
+    few calls after an idle set-up phase are not for millisecond-scale kernels."""
+    import torch
+    t0 = time.perf_counter()
+    i = 0
+    while i < min_calls or time.perf_counter() - t0 < seconds:
+        fn(i)
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def measure(prob, steps, warmup):
     """Time `steps` whole steps after `warmup` untimed ones, then the two kernels
     of the path on their own (each launched `steps` times back to back between
@@ -179,6 +194,7 @@ def measure(prob, steps, warmup):
     averages."""
     import torch
     from block_scaled_fp4_05_amd import moe_fp4
+    warm(prob.step)
     for i in range(warmup):
         prob.step(i)
     torch.cuda.synchronize()
@@ -194,9 +210,7 @@ def measure(prob, steps, warmup):
     region_ms = e0.elapsed_time(e1)
 
     def back_to_back(fn):
-        for i in range(3):
-            fn(i)
-        torch.cuda.synchronize()
+        warm(fn)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for i in range(steps):
@@ -238,9 +252,7 @@ def finalize_report(prob, steps):
     tokens = torch.empty((w.tokens, w.n), dtype=torch.float32, device=dev)
 
     def timed(fn):
-        for i in range(3):
-            fn(i)
-        torch.cuda.synchronize()
+        warm(fn)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for i in range(steps):
@@ -335,9 +347,7 @@ def swiglu_report(prob, steps):
     u_q, u_sf = torch.empty_like(h_q), torch.empty_like(h_sf)
 
     def timed(fn):
-        for i in range(3):
-            fn(i)
-        torch.cuda.synchronize()
+        warm(fn)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for i in range(steps):

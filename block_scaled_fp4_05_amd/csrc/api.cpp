@@ -19,7 +19,9 @@ using moe_fp4::GemmTile;
 namespace {
 
 constexpr int kAbiVersion = 2;
-constexpr int32_t kMaxExperts = 16384;  // the work-list prefix lives in LDS
+// The work-list tables (8 bytes per expert) live in LDS beside each kernel's
+// own buffers (at most 68 KB); 8192 experts keep every kernel within 160 KB.
+constexpr int32_t kMaxExperts = 8192;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 

@@ -60,10 +60,16 @@ struct WorkList {
   const int32_t* off;
 };
 
+// Items of an expert with cnt rows in this launch: ceil(cnt / bm) * n_tiles if
+// cnt is in the launch's row range, else none (an empty expert, or a
+// decreasing offset pair, a violated precondition, owns none either).
+__device__ __forceinline__ int32_t expert_items(const GemmArgs& p, int32_t cnt, int32_t bm) {
+  const bool take = cnt > 0 && cnt >= p.rows_lo && (p.rows_hi == 0 || cnt < p.rows_hi);
+  return take ? ((cnt + bm - 1) / bm) * p.n_tiles : 0;
+}
+
 // Fill the work-list tables (all NTHR threads of the workgroup take part; two
-// barriers inside).  An expert with cnt rows owns ceil(cnt / bm) * n_tiles
-// items; an empty expert (or a decreasing offset pair, a violated
-// precondition) owns none.  Returns the total item count.
+// barriers inside).  Returns the total item count.
 template <int NTHR>
 __device__ __forceinline__ int32_t build_worklist(const GemmArgs& p, int32_t bm, int32_t* prefix,
                                                   int32_t* offl, int32_t* wave_sum) {
@@ -77,7 +83,7 @@ __device__ __forceinline__ int32_t build_worklist(const GemmArgs& p, int32_t bm,
   int32_t local = 0;
   for (int e = beg; e < end; ++e) {
     const int32_t cnt = clamp_off(p.offsets[e + 1], m_total) - clamp_off(p.offsets[e], m_total);
-    local += cnt > 0 ? ((cnt + bm - 1) / bm) * p.n_tiles : 0;
+    local += expert_items(p, cnt, bm);
   }
   int32_t incl = local;
 #pragma unroll
@@ -95,7 +101,7 @@ __device__ __forceinline__ int32_t build_worklist(const GemmArgs& p, int32_t bm,
     const int32_t lo = clamp_off(p.offsets[e], m_total), hi = clamp_off(p.offsets[e + 1], m_total);
     offl[e] = lo;
     const int32_t cnt = hi - lo;
-    run += cnt > 0 ? ((cnt + bm - 1) / bm) * p.n_tiles : 0;
+    run += expert_items(p, cnt, bm);
   }
   if (tid == NTHR - 1) {
     int32_t total = 0;

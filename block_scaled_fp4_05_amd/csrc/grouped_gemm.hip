@@ -47,9 +47,20 @@ GemmTile choose_tile(int32_t num_experts, int64_t m_total, int64_t n, int64_t k,
   if (avg > 32) t.m_blocks = 4;
   else if (avg > 16) t.m_blocks = 2;
   // Experts this large are compute-bound: share dequantised operands in LDS.
-  if (avg >= 96) t = GemmTile{8, 8, 4, 1, 0, 1};
+  // When the work list leaves room for two 64 KB stages, experts with at least
+  // kBigRows rows take 256 x 256 items and the rest the per-wave kernel (two
+  // launches over disjoint experts, chosen on the device from the offsets);
+  // else every expert takes 128 x 128 items.
+  if (avg >= 96) t = big_lds(num_experts) <= kLdsBytes ? GemmTile{16, 16, 8, 1, 0, 2}
+                                                        : GemmTile{8, 8, 4, 1, 0, 1};
   if (k % 512 == 0) t.k_sub = 2;
   t.lds_scales = k % kSpan == 0 ? 1 : 0;
+  // "256x256!": every expert in 256 x 256 items, however few its rows.
+  if (env && env[0] == '2' && env[1] == '5' && env[2] == '6' && env[3] == 'x' && env[4] == '2' &&
+      env[5] == '5' && env[6] == '6' && env[7] == '!' && env[8] == '\0') {
+    if (big_lds(num_experts) <= kLdsBytes) t = GemmTile{16, 16, 8, 1, 0, 3};
+    return t;
+  }
   if (env && *env) {
     // "MxN" or "MxNxK", optionally followed by 'r' (weight scales through
     // registers rather than LDS): M rows per item, N columns per wave, K
@@ -72,6 +83,10 @@ GemmTile choose_tile(int32_t num_experts, int64_t m_total, int64_t n, int64_t k,
       t = GemmTile{8, 8, 4, 1, 0, 1};
       return t;
     }
+    if (ok && nv == 2 && v[0] == 256 && v[1] == 256 && !regs) {
+      if (big_lds(num_experts) <= kLdsBytes) t = GemmTile{16, 16, 8, 1, 0, 2};
+      return t;
+    }
     ok = ok && (v[0] == 16 || v[0] == 32 || v[0] == 64) && (v[1] == 32 || v[1] == 64);
     if (nv == 3)
       ok = ok && (v[2] == 256 || (v[2] == 512 && k % 512 == 0) ||
@@ -90,6 +105,7 @@ GemmTile choose_tile(int32_t num_experts, int64_t m_total, int64_t n, int64_t k,
 }
 
 int64_t gemm_lds_bytes(const GemmTile& t, int32_t num_experts) {
+  if (t.tiled >= 2) return (int64_t)big_lds(num_experts) + 16;
   if (t.tiled) return (int64_t)tiled_lds(num_experts) + 16;
   int64_t b = (int64_t)worklist_bytes(num_experts) + (int64_t)sizeof(int32_t) * t.waves;
   if (t.lds_scales) b += (int64_t)t.waves * (2 * 16 * 16 * t.n_blocks * 8 + 1024);
@@ -138,7 +154,26 @@ hipError_t launch_sl(const GemmArgs& p, const GemmTile& t, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
+// Per-wave tile for the experts below kBigRows rows when the large tile takes
+// the rest: 32-row items, 64 columns, the K step of the packed granule.
+GemmTile small_expert_tile(int64_t k) {
+  return GemmTile{2, 4, 4, k % 512 == 0 ? 2 : 1, k % kSpan == 0 ? 1 : 0, 0};
+}
+
 hipError_t launch_grouped_gemm(const GemmArgs& p, const GemmTile& t, hipStream_t stream) {
+  if (t.tiled == 3) return launch_grouped_gemm_big(p, stream);
+  if (t.tiled == 2) {
+    // Experts with kBigRows rows or more in 256 x 256 items, the rest per wave.
+    GemmArgs big = p, small = p;
+    big.rows_lo = kBigRows;
+    big.n_tiles = (int32_t)((p.n + 255) / 256);
+    hipError_t err = launch_grouped_gemm_big(big, stream);
+    if (err != hipSuccess) return err;
+    const GemmTile s = small_expert_tile(p.k);
+    small.rows_hi = kBigRows;
+    small.n_tiles = (int32_t)((p.n + 16 * s.n_blocks - 1) / (16 * s.n_blocks));
+    return s.lds_scales ? launch_sl<true>(small, s, stream) : launch_sl<false>(small, s, stream);
+  }
   if (t.tiled) return launch_grouped_gemm_tiled(p, stream);
   if (t.waves != 4 || p.k % (256 * t.k_sub) != 0) return hipErrorInvalidValue;
   if (t.lds_scales) {

@@ -1,0 +1,310 @@
+// NVFP4 grouped GEMM for gfx950, large-tile variant for the compute-bound end
+// of the grouped problem (prefill-sized experts and the dense case; "Peering
+// into the CUTLASS Kernel", section "Input Knowledge Required", item 4, with
+// the reuse argument of "Peering into the CUTLASS SharedStorage", section
+// "Why This Matters": larger tiles re-read less data per multiply-add).
+//
+// The exact path multiplies dequantised FP16 values on the FP16 MFMA.  A
+// workgroup of 8 wavefronts (two per SIMD) computes a 256 x 256 tile, each
+// wavefront a 128 x 64 piece with v_mfma_f32_32x32x16_f16 (8 accumulator tiles
+// of 32 x 32).  Per 64-element K stage every thread loads one operand row's 32
+// code bytes and 4 block-scale bytes (waves 0-3 activation rows, waves 4-7
+// weight rows; a register ring keeps PD stages of loads in flight), dequantises
+// it exactly to FP16 (fp4_device.h) and writes it to the next of two 64 KB LDS
+// stages while the MFMAs of the current stage run.  Each element is
+// dequantised once per workgroup; what the MFMAs read from LDS per stage (192
+// KB) and what the threads write (64 KB) stay under the MFMA time at 256 bytes
+// per clock, and the second wavefront of each SIMD issues while the first waits.
+// Items (expert, 256-row M-tile, 256-column N-tile) come from the device-side
+// work list, one per workgroup per round.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp4_device.h"
+#include "gemm_common.h"
+#include "launch.h"
+
+namespace moe_fp4 {
+namespace {
+
+constexpr int kBM = 256;                 // output rows per item
+constexpr int kBN = 256;                 // output columns per item
+constexpr int kBK = 64;                  // K elements per stage
+constexpr int kBThreads = 512;           // 8 wavefronts: 2 (rows) x 4 (columns)
+constexpr int kBRow = kBK * 2;           // one operand row of a stage in FP16
+constexpr int kBStage = (kBM + kBN) * kBRow;  // 64 KB
+
+__host__ __device__ constexpr size_t big_lds_bytes(int num_experts) {
+  return worklist_bytes(num_experts) + 2 * (size_t)kBStage;
+}
+
+// Row r of a stage is 8 chunks of 16 bytes (8 FP16 values); chunk q is stored at
+// position q ^ swz(r).  The lanes of one LDS access touch 8 or 16 consecutive
+// rows with one chunk index; swz is a bijection on every 8 aligned rows, and
+// with the row's parity (which half of a 256-byte bank line it lands in) on
+// every 16, so those lanes hit distinct banks either way.
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+__device__ __forceinline__ void put_chunk(uint8_t* stage, int row, int q, const half8_t& v) {
+  *reinterpret_cast<half8_t*>(stage + row * kBRow + 16 * (q ^ swz(row))) = v;
+}
+
+// Operand of v_mfma_f32_32x32x16_f16 for a 32-row block and K slice sl (16
+// elements): lane l reads row `row0 + l % 32`, K values 16*sl + 8*(l / 32) .. +7.
+__device__ __forceinline__ half8_t frag32(const uint8_t* stage, int row0, int lane, int sl) {
+  const int row = row0 + (lane & 31);
+  const int q = 2 * sl + (lane >> 5);
+  return *reinterpret_cast<const half8_t*>(stage + row * kBRow + 16 * (q ^ swz(row)));
+}
+
+typedef float float16_t __attribute__((ext_vector_type(16)));
+
+// One operand row's raw stage: 64 codes in two 16-byte pieces and 4 scale bytes.
+struct RowStage {
+  u32x4_t q0, q1;
+  uint32_t s;
+};
+
+// Dequantise chunk w (8 values) of a row's stage into LDS row `row`.
+__device__ __forceinline__ void dequant_chunk(uint8_t* stage, int row, const RowStage& r, int w) {
+  const half2_t sp = (w < 4) ? scale_pair_x2m8<false>(r.s) : scale_pair_x2m8<true>(r.s);
+  const _Float16 sc = sp[(w >> 1) & 1];
+  put_chunk(stage, row, w, dequant8(w < 4 ? r.q0[w & 3] : r.q1[w & 3], sc));
+}
+
+template <int PD>
+__global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_grouped_gemm_big(const GemmArgs p) {
+  static_assert(PD % 2 == 0, "stage ring must be even (LDS buffers alternate)");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  int32_t* prefix = reinterpret_cast<int32_t*>(smem);
+  int32_t* offl = prefix + (p.num_experts + 1);
+  __shared__ int32_t wave_sum[kBThreads / 64];
+  uint8_t* const stages = smem + worklist_bytes(p.num_experts);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;  // this wave's piece: rows 128*wm.., columns 64*wn..
+  // Loader role (uniform per wave): waves 0-3 load activation rows, 4-7 weight rows.
+  const bool is_w = wave >= 4;
+  const int lrow = tid & 255;
+  const int srow = (is_w ? kBM : 0) + lrow;  // the row this thread writes in a stage
+
+  const int32_t total_items = build_worklist<kBThreads>(p, kBM, prefix, offl, wave_sum);
+  const WorkList wl{prefix, offl};
+
+  const int nblk = gridDim.x, b = blockIdx.x;
+  const int32_t rounds = (total_items + nblk - 1) / nblk;
+  if (rounds == 0) return;
+  const int32_t last_items = total_items - (rounds - 1) * nblk;
+  const int32_t lb_full = logical_block(b, nblk, nblk);
+  const int32_t lb_last = logical_block(b, nblk, last_items);
+  const int32_t my_items = (rounds - 1) + (lb_last < last_items ? 1 : 0);
+
+  const int32_t n = (int32_t)p.n, kb = (int32_t)(p.k >> 1), nbk = (int32_t)(p.k >> 4);
+  const int32_t nst = (int32_t)(p.k / kBK);
+  const int32_t a_last = (int32_t)p.a_rows - 1;
+  // Packed weight layout: bytes of a 16-row block, and log2 of the stages per
+  // granule (a granule of 256 or 512 elements holds 4 or 8 stages of 64).
+  const int32_t pk_block = packed_block_bytes(packed_granule(p.k));
+  const int32_t pk_lg = packed_granule(p.k) == 512 ? 3 : 2;
+
+  int32_t from = 0;
+  for (int32_t j = 0; j < my_items; ++j) {
+    const int32_t item = j * nblk + (j == rounds - 1 ? lb_last : lb_full);
+    const ItemPos it = locate(item, from, wl, p, kBM, kBN, lane);
+    from = it.e;
+
+    // This thread's operand row: activation row `lrow` of the item, gathered
+    // through the row index (rows past the expert's end repeat its first row:
+    // computed, never stored), or weight row `lrow` (past n: out of range,
+    // reads zeros).
+    rsrc_t rq, rs;
+    uint32_t vq, vs, half = 16;
+    int32_t wrg = 0;  // packed weights: 16-row blocks in this wave's 64-row group
+    if (is_w) {
+      rq = make_rsrc(p.w_q + (int64_t)it.e * n * kb, (uint32_t)(n * kb));
+      rs = make_rsrc(p.w_sf + (int64_t)it.e * n * nbk, (uint32_t)(n * nbk));
+      const int32_t row = it.n0 + lrow;
+      if (p.w_packed) {
+        // This wave's 64 rows are one group of the packed layout; a thread's
+        // row is piece r of each 16-row block j of the group.  (A group wholly
+        // past n has no blocks: its rows read out of range.)
+        const int32_t grp0 = uniform(it.n0 + 64 * (wave - 4));
+        const int32_t left = grp0 < n ? (n - grp0) / 16 : 0;
+        wrg = left < 4 ? left : 4;
+        const int32_t jb = (row - grp0) >> 4, r = row & 15;
+        vq = row < n ? (uint32_t)(grp0 * kb + jb * pk_block + 16 * r) : kOutOfRange;
+        half = 1024;
+      } else {
+        vq = row < n ? (uint32_t)(row * kb) : kOutOfRange;
+      }
+      vs = row < n ? (uint32_t)(row * nbk) : kOutOfRange;
+    } else {
+      const int32_t r = it.row0 + (lrow < it.rows_valid ? lrow : 0);
+      int32_t src = p.a_row_index ? p.a_row_index[r] : r;
+      src = src < 0 ? 0 : (src > a_last ? a_last : src);
+      rq = make_rsrc(p.a_q, (uint32_t)(p.a_rows * kb));
+      rs = make_rsrc(p.a_sf, (uint32_t)(p.a_rows * nbk));
+      vq = (uint32_t)(src * kb);
+      vs = (uint32_t)(src * nbk);
+    }
+    // Byte offset of stage st's codes: row-major, 32 bytes per stage; packed
+    // (weight waves), two 16-byte pieces 1 KB apart in block j of granule t, at
+    // the position of sub-step s and lane group g of the packed order.
+    const bool wpk = is_w && p.w_packed;
+    auto q_off = [&](int32_t st) -> int32_t {
+      if (!wpk) return st * (kBK / 2);
+      const int32_t t = st >> pk_lg, m = st & ((1 << pk_lg) - 1);
+      const int32_t gg = m >> (pk_lg - 2), sub = m & ((1 << (pk_lg - 2)) - 1);
+      return t * wrg * pk_block + sub * 2048 + gg * 256;
+    };
+
+    // 2 x 4 accumulator tiles of 32 x 32: acc[wb][ab] holds weight rows (output
+    // columns) 32*wb .. +31 and activation rows 32*ab .. +31 of this wave's piece.
+    float16_t acc[2][4];
+#pragma unroll
+    for (int wb = 0; wb < 2; ++wb)
+#pragma unroll
+      for (int ab = 0; ab < 4; ++ab)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[wb][ab][i] = 0.0f;
+
+    // The ring: slot d holds the raw stage loaded PD stages before it is
+    // dequantised.  Stages past the last one load out of range (no traffic).
+    RowStage ring[PD];
+    auto load_stage = [&](int slot, int32_t st) {
+      const bool in = st < nst;
+      const int32_t kq = uniform(q_off(st)), ks = uniform(st * (kBK / 16));
+      const uint32_t oq = in ? vq : kOutOfRange, os = in ? vs : kOutOfRange;
+      ring[slot].q0 = __builtin_amdgcn_raw_buffer_load_b128(rq, oq, kq, 0);
+      ring[slot].q1 = __builtin_amdgcn_raw_buffer_load_b128(rq, oq + half, kq, 0);
+      ring[slot].s = __builtin_amdgcn_raw_buffer_load_b32(rs, os, ks, 0);
+    };
+
+    // MFMA operands of one 16-element K slice: fw[2] weight and fa[4] activation
+    // blocks of 32 rows of this wave's piece; two slices in flight.
+    half8_t fw[2][2], fa[2][4];
+    // Operand read i (0..5) of slice sl, in the order the slice's MFMAs first
+    // need them: fw[0], fa[0..3], fw[1].
+    auto read_one = [&](const uint8_t* stage, int sl, int i) {
+      const int sk = sl & 3, f = sl & 1;
+      if (i == 0) fw[f][0] = frag32(stage, kBM + 64 * wn, lane, sk);
+      else if (i < 5) fa[f][i - 1] = frag32(stage, 128 * wm + 32 * (i - 1), lane, sk);
+      else fw[f][1] = frag32(stage, kBM + 64 * wn + 32, lane, sk);
+    };
+    // MFMA i (0..7) of slice sl: weight block i / 4, activation block i % 4.
+    auto mfma_one = [&](int sl, int i) {
+      const int wb = i >> 2, ab = i & 3, f = sl & 1;
+      acc[wb][ab] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fw[f][wb], fa[f][ab], acc[wb][ab], 0, 0, 0);
+    };
+
+#pragma unroll
+    for (int d = 0; d < PD; ++d) {
+      load_stage(d, d);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int w = 0; w < 8; ++w) dequant_chunk(stages, srow, ring[0], w);
+    load_stage(0, PD);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 6; ++i) read_one(stages, 0, i);
+
+    // Stage st (data in buffer `cur`, slice 0's operands already in registers),
+    // issued in a fixed order, one MFMA per step:
+    //   slices 0-2 (steps 0-23): step m issues MFMA m % 8 of slice m / 8; the
+    //       first 6 steps of each slice also read one operand of the next slice,
+    //       and every third step dequantises one 16-byte chunk of stage st+1
+    //       (from the ring) into `nxt`; then the ring slot is reloaded with stage
+    //       st+1+PD;
+    //   barrier: stage st+1 is in `nxt`, and every read of `cur` is done;
+    //   slice 3 (steps 24-31): the same, reading stage st+1's slice 0 from `nxt`.
+    // `cur` is rewritten (with stage st+2) only in the next stage, after this
+    // barrier, so one barrier per stage orders every LDS access.  The last stage
+    // dequantises the ring's out-of-range loads (zeros) into `nxt`, unused.
+    for (int32_t st0 = 0; st0 < nst; st0 += PD) {
+#pragma unroll
+      for (int d = 0; d < PD; ++d) {
+        const int32_t st = st0 + d;
+        const uint8_t* cur = stages + (d & 1) * kBStage;  // PD is even: d & 1 == st & 1
+        uint8_t* nxt = stages + ((d + 1) & 1) * kBStage;
+        const int kSlot = (d + 1) % PD;  // holds stage st + 1
+#pragma unroll
+        for (int m = 0; m < 24; ++m) {
+          const int sl = m >> 3, i = m & 7;
+          mfma_one(sl, i);
+          if (i < 6) read_one(cur, sl + 1, i);
+          if (m % 3 == 0) dequant_chunk(nxt, srow, ring[kSlot], m / 3);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        load_stage(kSlot, st + 1 + PD);
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          mfma_one(3, i);
+          if (i < 6) read_one(nxt, 4, i);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    // The next item's first stage rewrites buffer 0, which the last slice 3
+    // read from.
+    __syncthreads();
+
+    // Epilogue: lane l holds activation row 128*wm + 32*ab + l % 32 and, per
+    // accumulator quad q, the 4 output columns 64*wn + 32*wb + 8q + 4*(l / 32)
+    // .. +3.  The store resource covers exactly the item's valid rows, so rows
+    // past the expert's end are dropped; column quads past n are skipped.
+    {
+      typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+      const int32_t ldo = (int32_t)p.ldo;
+      const rsrc_t o = make_rsrc(p.out + (int64_t)it.row0 * ldo,
+                                 (uint32_t)((int64_t)it.rows_valid * ldo * 2));
+      const int r32 = lane & 31, h = lane >> 5;
+#pragma unroll
+      for (int wb = 0; wb < 2; ++wb) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int32_t col = it.n0 + 64 * wn + 32 * wb + 8 * q + 4 * h;
+          if (col < n) {
+#pragma unroll
+            for (int ab = 0; ab < 4; ++ab) {
+              const float16_t& v = acc[wb][ab];
+              const bf16x4_t bv = {(__bf16)(v[4 * q] * it.alpha), (__bf16)(v[4 * q + 1] * it.alpha),
+                                   (__bf16)(v[4 * q + 2] * it.alpha), (__bf16)(v[4 * q + 3] * it.alpha)};
+              const uint32_t off = (uint32_t)(((128 * wm + 32 * ab + r32) * ldo + col) * 2);
+              __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, bv), o, off, 0, 0);
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+size_t big_lds(int32_t num_experts) { return big_lds_bytes(num_experts); }
+
+hipError_t launch_grouped_gemm_big(const GemmArgs& p, hipStream_t stream) {
+  // K is a multiple of 256, so the stage count (K / 64) is a multiple of the ring.
+  constexpr int PD = 2;
+  auto kern = k_grouped_gemm_big<PD>;
+  const size_t lds = big_lds_bytes(p.num_experts);
+  if (lds > kLdsBytes) return hipErrorInvalidValue;  // the host picks this tile only if it fits
+  int resident = 0;
+  hipError_t err = resident_groups(kern, kBThreads, lds, &resident);
+  if (err != hipSuccess) return err;
+  // Upper bound on the number of items: the host does not see the offsets.
+  const int64_t max_mtiles = p.m_total / kBM + (p.m_total < p.num_experts ? p.m_total : p.num_experts);
+  const int64_t max_items = max_mtiles * p.n_tiles;
+  int64_t grid = resident;
+  if (max_items < grid) grid = max_items;
+  if (grid < 1) grid = 1;
+  grid = (grid + kXcds - 1) / kXcds * kXcds;  // whole rounds over the XCDs
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBThreads), lds, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace moe_fp4

@@ -22,7 +22,10 @@ struct GemmTile {
   int waves;
   int k_sub;
   int lds_scales;  // weight block scales staged through LDS (needs k % 2048 == 0)
-  int tiled;       // workgroup-tiled kernel (128 x 128 items, operands shared in LDS)
+  int tiled;       // workgroup-tiled kernel, operands shared in LDS: 1 = 128 x 128
+                   // items (grouped_gemm_tiled.hip); 2 = 256 x 256 items
+                   // (grouped_gemm_big.hip) for experts of kBigRows rows or more
+                   // and the per-wave kernel for the rest; 3 = 256 x 256 for all
 };
 
 constexpr int kKStep = 256;  // K granularity the kernels require
@@ -82,6 +85,11 @@ struct GemmArgs {
   int32_t num_experts;
   int32_t n_tiles;   // ceil(n / (16 * n_blocks))
   int32_t w_packed;  // w_q is in the packed layout
+  // Experts this launch covers, by row count: rows_lo <= rows, and rows <
+  // rows_hi unless rows_hi is 0 (so a zeroed GemmArgs covers every expert).
+  // Launches over disjoint ranges write disjoint output rows.
+  int32_t rows_lo;
+  int32_t rows_hi;
   // Finalize epilogue only (moe_grouped_gemm_fp4_finalize): routed row r adds
   // row_weight[r] * its result into FP32 row out_token[r] of fin_out.
   const int32_t* out_token;
@@ -111,5 +119,16 @@ hipError_t launch_grouped_gemm_swiglu(const GemmArgs& args, const GemmTile& tile
 // Workgroup-tiled kernel (grouped_gemm_tiled.hip): 128 x 128 items, 4 waves.
 hipError_t launch_grouped_gemm_tiled(const GemmArgs& args, hipStream_t stream);
 size_t tiled_lds(int32_t num_experts);
+
+// Large-tile kernel (grouped_gemm_big.hip): 256 x 256 items, 4 waves of 128 x 128.
+hipError_t launch_grouped_gemm_big(const GemmArgs& args, hipStream_t stream);
+size_t big_lds(int32_t num_experts);
+
+// LDS a workgroup may use on gfx950.
+constexpr size_t kLdsBytes = 160 * 1024;
+
+// Rows from which an expert takes the 256 x 256 tile when the problem is split
+// by expert size (GemmTile.tiled == 2).
+constexpr int32_t kBigRows = 256;
 
 }  // namespace moe_fp4

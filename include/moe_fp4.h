@@ -147,7 +147,7 @@ int moe_fp4_quantize(const void* x, int in_dtype, int64_t rows, int64_t k, int64
  * inputs give the same output bits (no atomics in the accumulation).
  * Errors: NULL, SHAPE (num_experts < 1, m_total < 0, n < 1, k < 1, ldo < n,
  * a_rows < m_total without an index, a_rows < 1 with m_total > 0),
- * ALIGN, UNSUPPORTED (n % 16, k % 256, num_experts > 16384, sizes whose byte
+ * ALIGN, UNSUPPORTED (n % 16, k % 256, num_experts > 8192, sizes whose byte
  * offsets need more than 32 bits: n * k/2 or a_rows * k/2 >= 2^31 - 4096,
  * m_total >= 2^29 - 1024, ldo > 2^23), HIP.
  */

@@ -55,8 +55,8 @@ def test_plan_picks_tiles_by_rows_per_expert(monkeypatch):
     monkeypatch.delenv("MOE_FP4_TILE", raising=False)
     assert m.plan(256, 4096, 512, 6144)["tile_m"] == 16
     assert m.plan(256, 8192, 6144, 256)["tile_m"] == 32
-    assert m.plan(1, 8192, 8192, 8192)["tile_m"] == 128   # compute-bound: workgroup tile
-    assert m.plan(256, 32768, 512, 6144)["tile_m"] == 128
+    assert m.plan(1, 8192, 8192, 8192)["tile_m"] == 256   # compute-bound: large workgroup tile
+    assert m.plan(256, 32768, 512, 6144)["tile_m"] == 256  # large experts in 256-row items
     assert m.plan(256, 16384, 512, 6144)["tile_m"] == 64
     monkeypatch.setenv("MOE_FP4_TILE", "64x32")
     p = m.plan(256, 4096, 512, 6144)
@@ -64,6 +64,12 @@ def test_plan_picks_tiles_by_rows_per_expert(monkeypatch):
     monkeypatch.setenv("MOE_FP4_TILE", "128x128")
     p = m.plan(256, 4096, 512, 6144)
     assert (p["tile_m"], p["tile_n"], p["k_step"]) == (128, 128, 64)
+    monkeypatch.setenv("MOE_FP4_TILE", "256x256")
+    p = m.plan(256, 4096, 512, 6144)
+    assert (p["tile_m"], p["tile_n"], p["k_step"], p["lds_bytes"]) == (256, 256, 64, 2064 + 131072 + 16)
+    # The large tile needs 128 KB of stages beside the work list: too many experts
+    # to fit it keep the default choice.
+    assert m.plan(8192, 512 * 8192, 512, 6144)["tile_m"] == 128
     monkeypatch.setenv("MOE_FP4_TILE", "48x64")  # unsupported -> ignored
     assert m.plan(256, 4096, 512, 6144)["tile_m"] == 16
 
@@ -121,7 +127,7 @@ def _g(**kw):
     (dict(w_sf=None), 1), (dict(w_scale=None), 1), (dict(off=None), 1), (dict(out=None), 1),
     (dict(E=0), 2), (dict(m=-1), 2), (dict(n=0), 2), (dict(k=0), 2), (dict(ldo=32), 2),
     (dict(a_rows=63), 2), (dict(a_rows=0, idx=P16), 2), (dict(a_rows=-1), 2),
-    (dict(n=24, ldo=24), 4), (dict(k=128), 4), (dict(k=320), 4), (dict(E=20000), 4),
+    (dict(n=24, ldo=24), 4), (dict(k=128), 4), (dict(k=320), 4), (dict(E=20000), 4), (dict(E=8193), 4),
     (dict(a_q=P16 + 8), 3), (dict(w_sf=P16 + 4), 3), (dict(out=P16 + 8), 3), (dict(ldo=68), 3),
     (dict(off=P16 + 2), 3), (dict(idx=P16 + 2), 3), (dict(a_scale=P16 + 1), 3),
 ])

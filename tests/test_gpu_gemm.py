@@ -84,7 +84,7 @@ def _check_rows(got_bits, P, rows_sel=None, a_row_index=None, label=""):
     return float(err.max()) if err.size else 0.0
 
 
-TILES = ["16x64", "32x64", "64x64", "16x32", "32x32", "64x32", "128x128"]
+TILES = ["16x64", "32x64", "64x64", "16x32", "32x32", "64x32", "128x128", "256x256", "256x256!"]
 
 
 @pytest.mark.parametrize("tile", TILES)
@@ -240,6 +240,24 @@ PACKED_CASES = [
     (1, [150], 96, 2048),
     (2, [100, 120], 80, 768),
 ]
+
+
+# (E, rows per expert, n, k) for the workgroup tiles: several M- and N-tiles per
+# expert with ragged last tiles, an empty expert, packed groups of 16..48 rows at n.
+WG_CASES = [(2, [300, 520], 320, 1024), (3, [257, 0, 40], 272, 512), (1, [600], 528, 768)]
+
+
+@pytest.mark.parametrize("tile", ["128x128", "256x256", "256x256!"])
+@pytest.mark.parametrize("case", range(len(WG_CASES)))
+def test_workgroup_tiles_several_tiles_per_expert(case, tile):
+    E, rows, n, k = WG_CASES[case]
+    P = _random_problem(E, rows, n, k, 760 + case, a_rows=sum(rows) + 5)
+    idx = np.random.default_rng(761 + case).integers(0, sum(rows) + 5, P["m_total"]).astype(np.int32)
+    say(f"gemm tile={tile} E={E} rows={rows} n={n} k={k}")
+    ref = _gpu_gemm(P, a_row_index=idx, extra_rows=2, tile=tile)
+    _check_rows(ref, P, a_row_index=idx, label=f"{tile} case {case}")
+    got = _gpu_gemm(P, a_row_index=idx, extra_rows=2, tile=tile, packed=True)
+    assert np.array_equal(got, ref)
 
 
 @pytest.mark.parametrize("case", range(len(PACKED_CASES)))
