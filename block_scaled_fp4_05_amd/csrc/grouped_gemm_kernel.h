@@ -169,9 +169,11 @@ __device__ __forceinline__ uint32_t mul24(int32_t a, int32_t b) {
   return __umul24((uint32_t)a, (uint32_t)b);
 }
 
+// Weight half of item_loads: the expert's weight resources and the lane's
+// weight and scale-line offsets (no dependence on the row index).
 template <int MB, int NBW, int KSUB, bool PK, bool SW>
-__device__ __forceinline__ void item_loads(const ItemPos& it, const GemmArgs& p, int lane,
-                                           const uint32_t (&rows)[MB], ItemLoads<MB, NBW>& ld) {
+__device__ __forceinline__ void item_loads_w(const ItemPos& it, const GemmArgs& p, int lane,
+                                             ItemLoads<MB, NBW>& ld) {
   const int c = lane & 15, g = lane >> 4;
   // 32-bit offsets: the host guarantees n * k/2 and a_rows * k/2 < 2^31.
   const int32_t n = (int32_t)p.n, kb = (int32_t)(p.k >> 1), nbk = (int32_t)(p.k >> 4);
@@ -209,6 +211,15 @@ __device__ __forceinline__ void item_loads(const ItemPos& it, const GemmArgs& p,
     const int r8 = lane >> 3, slot = lane & 7;
     ld.sl_voff = mul24(it.n0 + r8, nbk) + 16 * (slot ^ r8);
   }
+}
+
+// Activation half of item_loads: the lane's activation row offsets, from its
+// row-index entries `rows`.
+template <int MB, int NBW, int KSUB>
+__device__ __forceinline__ void item_loads_a(const ItemPos& it, const GemmArgs& p, int lane,
+                                             const uint32_t (&rows)[MB], ItemLoads<MB, NBW>& ld) {
+  const int c = lane & 15, g = lane >> 4;
+  const int32_t kb = (int32_t)(p.k >> 1), nbk = (int32_t)(p.k >> 4);
   const int32_t a_last = (int32_t)p.a_rows - 1;
 #pragma unroll
   for (int ib = 0; ib < MB; ++ib) {
@@ -218,6 +229,13 @@ __device__ __forceinline__ void item_loads(const ItemPos& it, const GemmArgs& p,
     ld.a_voff[ib] = mul24(mine, kb) + 32 * KSUB * g;
     ld.as_voff[ib] = mul24(mine, nbk) + 4 * KSUB * g;
   }
+}
+
+template <int MB, int NBW, int KSUB, bool PK, bool SW>
+__device__ __forceinline__ void item_loads(const ItemPos& it, const GemmArgs& p, int lane,
+                                           const uint32_t (&rows)[MB], ItemLoads<MB, NBW>& ld) {
+  item_loads_w<MB, NBW, KSUB, PK, SW>(it, p, lane, ld);
+  item_loads_a<MB, NBW, KSUB>(it, p, lane, rows, ld);
 }
 
 // The KSUB scale dwords of one lane, in one load.
@@ -254,7 +272,10 @@ struct LineCopy {
 // in-flight load still reads.  With SL, the stage first copies the 128-byte
 // scale lines of the item's 16*NBW weight rows for its span into LDS, or, if
 // it starts no span, issues the same copies out of range into the sink.
-template <int MB, int NBW, int KSUB, bool SL, bool PK, bool SW>
+// PART 0 issues everything; 1 only the weight side (line copies, codes, scales),
+// 2 only the activation side (the kernel's first stage issues 1, then 2, so the
+// weight loads need not wait for the row index).
+template <int MB, int NBW, int KSUB, bool SL, bool PK, bool SW, int PART = 0>
 __device__ __forceinline__ void issue_loads(Stage<MB, NBW, KSUB>& st, const ItemLoads<MB, NBW>& it,
                                             const rsrc_t& a_rs, const rsrc_t& as_rs, int32_t kst,
                                             const LineCopy& lc, int32_t n, int32_t nbk) {
@@ -263,7 +284,7 @@ __device__ __forceinline__ void issue_loads(Stage<MB, NBW, KSUB>& st, const Item
   constexpr int32_t kBlock = 16 * 128 * KSUB;
   const int32_t left = (n - it.n0) >> 4;
   const int32_t wk = PK ? (left < NBW ? left : NBW) * kBlock : 0;
-  if constexpr (SL) {
+  if constexpr (SL && PART != 2) {
     const bool on = lc.span >= 0;
     const int32_t soff = uniform(on ? lc.span * 128 : 0);
 #pragma unroll
@@ -283,23 +304,27 @@ __device__ __forceinline__ void issue_loads(Stage<MB, NBW, KSUB>& st, const Item
   // consecutive bytes of the row; packed: 1 KB apart (one load instruction
   // of the wavefront reads 1 KB of consecutive bytes).
   constexpr uint32_t kS = PK ? 2048u : 32u, kH = PK ? 1024u : 16u;
+  if constexpr (PART != 2) {
 #pragma unroll
-  for (int jb = 0; jb < NBW; ++jb) {
+    for (int jb = 0; jb < NBW; ++jb) {
 #pragma unroll
-    for (int s = 0; s < KSUB; ++s) {
-      st.w[jb][s][0] = __builtin_amdgcn_raw_buffer_load_b128(it.w, it.w_voff[jb] + kS * s, qw, 0);
-      st.w[jb][s][1] = __builtin_amdgcn_raw_buffer_load_b128(it.w, it.w_voff[jb] + kS * s + kH, qw, 0);
+      for (int s = 0; s < KSUB; ++s) {
+        st.w[jb][s][0] = __builtin_amdgcn_raw_buffer_load_b128(it.w, it.w_voff[jb] + kS * s, qw, 0);
+        st.w[jb][s][1] = __builtin_amdgcn_raw_buffer_load_b128(it.w, it.w_voff[jb] + kS * s + kH, qw, 0);
+      }
+      if constexpr (!SL) load_scales<KSUB>(st.ws[jb], it.ws, it.ws_voff[jb], sk);
     }
-    if constexpr (!SL) load_scales<KSUB>(st.ws[jb], it.ws, it.ws_voff[jb], sk);
   }
+  if constexpr (PART != 1) {
 #pragma unroll
-  for (int ib = 0; ib < MB; ++ib) {
+    for (int ib = 0; ib < MB; ++ib) {
 #pragma unroll
-    for (int s = 0; s < KSUB; ++s) {
-      st.a[ib][s][0] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, it.a_voff[ib] + 32u * s, qk, 0);
-      st.a[ib][s][1] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, it.a_voff[ib] + 32u * s + 16u, qk, 0);
+      for (int s = 0; s < KSUB; ++s) {
+        st.a[ib][s][0] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, it.a_voff[ib] + 32u * s, qk, 0);
+        st.a[ib][s][1] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, it.a_voff[ib] + 32u * s + 16u, qk, 0);
+      }
+      load_scales<KSUB>(st.as[ib], as_rs, it.as_voff[ib], sk);
     }
-    load_scales<KSUB>(st.as[ib], as_rs, it.as_voff[ib], sk);
   }
 }
 
@@ -764,11 +789,11 @@ void k_grouped_gemm(const GemmArgs p) {
   int32_t ld_round = 0, ld_st = 0, cp_round = 0, cp_st = 0;
   // Row-index entries: of the item being started (first item), then of nx.
   const rsrc_t idx_rs = make_rsrc(p.a_row_index, p.a_row_index ? (uint32_t)(4 * m_total) : 0u);
-  uint32_t nrow[MB];
+  uint32_t nrow[MB], frow[MB];  // frow: the first item's entries, for its first stage
   ld_pos = locate(item_of(0), 0, wl, p, 16 * MB, kItemCols, lane);
 #pragma unroll
-  for (int ib = 0; ib < MB; ++ib) nrow[ib] = row_index_load(idx_rs, ld_pos, ib, c);
-  item_loads<MB, NBW, KSUB, PK, SW>(ld_pos, p, lane, nrow, l[0]);
+  for (int ib = 0; ib < MB; ++ib) frow[ib] = row_index_load(idx_rs, ld_pos, ib, c);
+  item_loads_w<MB, NBW, KSUB, PK, SW>(ld_pos, p, lane, l[0]);
   // Finalize: each row's destination token and routing weight, fetched like
   // the row-index entries (ntok/nwt: of the item being started, then of nx)
   // and carried per register stage to the item's epilogue (ftok/fwt).
@@ -882,7 +907,12 @@ void k_grouped_gemm(const GemmArgs p) {
   };
 
   uint32_t wsd[NBW][KSUB];
-  issue_loads<MB, NBW, KSUB, SL, PK, SW>(s[0], l[0], a_rs, as_rs, ld_st, line_copy(ld_round, ld_st), n, nbk);
+  // The first stage: the weight side at once; the activation side once the row
+  // index has arrived (the weight loads must not wait for it).
+  issue_loads<MB, NBW, KSUB, SL, PK, SW, 1>(s[0], l[0], a_rs, as_rs, ld_st, line_copy(ld_round, ld_st), n, nbk);
+  __builtin_amdgcn_sched_barrier(0);
+  item_loads_a<MB, NBW, KSUB>(ld_pos, p, lane, frow, l[0]);
+  issue_loads<MB, NBW, KSUB, SL, PK, SW, 2>(s[0], l[0], a_rs, as_rs, ld_st, line_copy(ld_round, ld_st), n, nbk);
 #pragma unroll
   for (int r = 1; r < R - 1; ++r) issue(r, r - 1, r);
   bool done = false;
