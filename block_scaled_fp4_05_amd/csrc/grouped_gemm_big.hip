@@ -252,33 +252,50 @@ void k_grouped_gemm_big(const GemmArgs p) {
     // read from.
     __syncthreads();
 
-    // Epilogue: lane l holds activation row 128*wm + 32*ab + l % 32 and, per
-    // accumulator quad q, the 4 output columns 64*wn + 32*wb + 8q + 4*(l / 32)
-    // .. +3.  The store resource covers exactly the item's valid rows, so rows
-    // past the expert's end are dropped; column quads past n are skipped.
+    // Epilogue, staged through LDS (both stage buffers are free after the last
+    // barrier; the 256 x 256 BF16 tile is exactly their 128 KB).  Lane l holds
+    // activation row 128*wm + 32*ab + l % 32 and, per accumulator quad q, the 4
+    // output columns 64*wn + 32*wb + 8q + 4*(l / 32) .. +3: written to LDS row
+    // by row (512 bytes, 16-byte chunk c at position c ^ (row % 32)), then read
+    // back so that each wave stores two whole 512-byte row segments per
+    // instruction.  Rows past the expert's end fall outside the store resource;
+    // 8-column chunks past n get an out-of-range offset.
     {
       typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-      const int32_t ldo = (int32_t)p.ldo;
-      const rsrc_t o = make_rsrc(p.out + (int64_t)it.row0 * ldo,
-                                 (uint32_t)((int64_t)it.rows_valid * ldo * 2));
+      constexpr int kTileRow = 2 * kBN;  // bytes
+      uint8_t* const tile = stages;
       const int r32 = lane & 31, h = lane >> 5;
 #pragma unroll
       for (int wb = 0; wb < 2; ++wb) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int32_t col = it.n0 + 64 * wn + 32 * wb + 8 * q + 4 * h;
-          if (col < n) {
+        for (int ab = 0; ab < 4; ++ab) {
+          const int row = 128 * wm + 32 * ab + r32;
 #pragma unroll
-            for (int ab = 0; ab < 4; ++ab) {
-              const float16_t& v = acc[wb][ab];
-              const bf16x4_t bv = {(__bf16)(v[4 * q] * it.alpha), (__bf16)(v[4 * q + 1] * it.alpha),
-                                   (__bf16)(v[4 * q + 2] * it.alpha), (__bf16)(v[4 * q + 3] * it.alpha)};
-              const uint32_t off = (uint32_t)(((128 * wm + 32 * ab + r32) * ldo + col) * 2);
-              __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, bv), o, off, 0, 0);
-            }
+          for (int q = 0; q < 4; ++q) {
+            const float16_t& v = acc[wb][ab];
+            const bf16x4_t bv = {(__bf16)(v[4 * q] * it.alpha), (__bf16)(v[4 * q + 1] * it.alpha),
+                                 (__bf16)(v[4 * q + 2] * it.alpha), (__bf16)(v[4 * q + 3] * it.alpha)};
+            const int chunk = 8 * wn + 4 * wb + q;
+            *reinterpret_cast<u32x2_t*>(tile + row * kTileRow + 16 * (chunk ^ (row & 31)) + 8 * h) =
+                __builtin_bit_cast(u32x2_t, bv);
           }
         }
       }
+      __syncthreads();
+      const int32_t ldo = (int32_t)p.ldo;
+      const rsrc_t o = make_rsrc(p.out + (int64_t)it.row0 * ldo,
+                                 (uint32_t)((int64_t)it.rows_valid * ldo * 2));
+      const int chunk = tid & 31, r0 = tid >> 5;  // 16 rows per pass of the workgroup
+      const bool col_ok = it.n0 + 8 * chunk < n;
+#pragma unroll
+      for (int i = 0; i < kBM / 16; ++i) {
+        const int row = r0 + 16 * i;
+        const u32x4_t d = *reinterpret_cast<const u32x4_t*>(tile + row * kTileRow + 16 * (chunk ^ (row & 31)));
+        const uint32_t off = col_ok ? (uint32_t)((row * ldo + it.n0 + 8 * chunk) * 2) : kOutOfRange;
+        __builtin_amdgcn_raw_buffer_store_b128(d, o, off, 0, 0);
+      }
+      // The next item's first stage rewrites these buffers.
+      __syncthreads();
     }
   }
 }

@@ -243,8 +243,10 @@ PACKED_CASES = [
 
 
 # (E, rows per expert, n, k) for the workgroup tiles: several M- and N-tiles per
-# expert with ragged last tiles, an empty expert, packed groups of 16..48 rows at n.
-WG_CASES = [(2, [300, 520], 320, 1024), (3, [257, 0, 40], 272, 512), (1, [600], 528, 768)]
+# expert with ragged last tiles, an empty expert, packed groups of 16..48 rows at n,
+# and experts on both sides of the size split (96 rows: large tile from there on).
+WG_CASES = [(2, [300, 520], 320, 1024), (3, [257, 0, 40], 272, 512), (1, [600], 528, 768),
+            (5, [95, 96, 97, 0, 1], 192, 512)]
 
 
 @pytest.mark.parametrize("tile", ["128x128", "256x256", "256x256!"])
