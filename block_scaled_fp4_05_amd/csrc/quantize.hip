@@ -7,18 +7,20 @@
 // definition, stated in moe_fp4.h.
 //
 // Kernels, in stream order:
-//   DYNAMIC: reset -> amax -> quantize      STATIC: quantize
-// The dynamic tensor scale is reduced in the caller's tensor_scale float
-// itself, so no scratch memory is needed.  Since g = fl(amax / 2688) is a
-// non-decreasing function of amax, the maximum of the per-workgroup values
-// fl(amax_wg / 2688) is g itself: each workgroup folds its own value in with
-// one integer atomic max on the float's bit pattern (signed order agrees with
-// float order for non-negative floats).  The reset writes -0.0 (bit pattern
-// INT_MIN), below every non-negative pattern, and a workgroup whose elements
-// are all zero contributes nothing, so -0.0 surviving the amax pass means an
-// all-zero tensor, for which g = 1; the quantiser reads it as 1 and writes 1.
-// The reset is a kernel rather than a memset so the sequence can be captured
-// in a graph.
+//   DYNAMIC: amax -> quantize      STATIC: quantize
+// The dynamic tensor scale needs the whole matrix's amax before any block can
+// be encoded, so it takes two launches; it needs no scratch memory, no atomics
+// and no reset launch.  Since g = fl(amax / 2688) is a non-decreasing function
+// of amax, the maximum of the per-workgroup values fl(amax_wg / 2688) is g
+// itself (0 for an all-zero matrix, for which g = 1).  The quantise launch is
+// laid out so that its workgroup w writes, in its first pass, the codes of
+// blocks [256 w, 256 w + 256): 2 KB of q that no other workgroup touches.  The
+// amax launch writes its P partial values into the first P floats of every
+// such 2 KB piece (P <= 512 workgroups, at most 2048 pieces); each quantise
+// workgroup reduces the copy in its own piece, and only after a barrier that
+// follows the reduction does it overwrite the piece with codes.  Workgroup 0
+// also publishes g to the caller's tensor_scale.  A matrix of fewer than 256
+// blocks takes one workgroup in each launch and one partial value.
 //
 // One thread quantises one 16-element block: 32 (BF16) or 64 (FP32) bytes in,
 // 8 bytes of codes and 1 scale byte out, consecutive threads on consecutive
@@ -62,12 +64,6 @@ __device__ __forceinline__ void load_block16(const void* x, I row, int64_t ld_x,
   }
 }
 
-constexpr uint32_t kNoAmax = 0x80000000u;  // -0.0f: "no non-zero element seen"
-
-__global__ void k_amax_reset(float* ts) {
-  if (blockIdx.x == 0 && threadIdx.x == 0) *reinterpret_cast<uint32_t*>(ts) = kNoAmax;
-}
-
 __global__ void k_set_one(float* ts) {
   if (blockIdx.x == 0 && threadIdx.x == 0) *ts = 1.0f;
 }
@@ -75,12 +71,35 @@ __global__ void k_set_one(float* ts) {
 // Blocks per thread per iteration of the amax pass: all their loads are in
 // flight before the reduction.
 constexpr int kAmaxBlocks = 4;
+// Blocks of one quantise workgroup's first pass, and the floats of q they
+// cover (8 bytes of codes per block): room for this many partial values.
+constexpr int kPiece = kThreads;
+constexpr int kPieceFloats = kPiece * 8 / 4;
+// Launch limits of the dynamic path: at most kMaxPartials amax workgroups and
+// kMaxPieces quantise workgroups, so the amax launch writes at most
+// kMaxPartials * kMaxPieces floats of partial values.
+constexpr int kMaxPartials = kPieceFloats;
+constexpr int kMaxPieces = 2048;
+
+// Block-wide maximum of one float per thread (all threads must call it).
+__device__ __forceinline__ float block_max(float m, float* wave_max) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
+  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = m;
+  __syncthreads();
+  float r = wave_max[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) r = fmaxf(r, wave_max[w]);
+  return r;
+}
 
 // I: the index type (32-bit whenever rows * k/16 fits, which avoids 64-bit
-// division in the index arithmetic).
+// division in the index arithmetic).  Workgroup p reduces its share of the
+// blocks to fl(amax / 2688) (0 if all its elements are 0) and stores it as
+// float p of each of the `pieces` 2 KB pieces at the start of q.
 template <int DT, typename I>
 __global__ __launch_bounds__(kThreads) void k_amax(const void* x, int64_t rows, int64_t k,
-                                                   int64_t ld_x, float* ts) {
+                                                   int64_t ld_x, float* partials, int pieces) {
   __shared__ float wave_max[kThreads / 64];
   const I nb = (I)(k / 16);
   const I total = (I)rows * nb;
@@ -101,39 +120,34 @@ __global__ __launch_bounds__(kThreads) void k_amax(const void* x, int64_t rows, 
 #pragma unroll
       for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[j][i]));
   }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
-  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float wg = wave_max[0];
-#pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) wg = fmaxf(wg, wave_max[w]);
-    if (wg > 0.0f) {
-      const float g = wg / 2688.0f;  // IEEE division, rounded to nearest even
-      atomicMax(reinterpret_cast<int*>(ts), __builtin_bit_cast(int, g));
-    }
-  }
-}
-
-// Tensor scale: the reduced value (DYNAMIC; -0.0 means all-zero input, g = 1)
-// or the caller's calibrated value (STATIC).
-template <bool DYN>
-__device__ __forceinline__ float tensor_scale_of(const float* ts) {
-  const float t = *ts;
-  if (!DYN) return t;
-  return __builtin_bit_cast(uint32_t, t) == kNoAmax ? 1.0f : t;
+  const float wg = block_max(m, wave_max);
+  const float g = wg / 2688.0f;  // IEEE division, rounded to nearest even (0 stays 0)
+  for (int w = threadIdx.x; w < pieces; w += kThreads)
+    partials[(int64_t)w * kPieceFloats + blockIdx.x] = g;
 }
 
 template <int DT, bool DYN, typename I>
 __global__ __launch_bounds__(kThreads) void k_quantize(const void* x, int64_t rows, int64_t k,
                                                        int64_t ld_x, uint8_t* q, uint8_t* sf,
-                                                       const float* ts) {
-  const float g = tensor_scale_of<DYN>(ts);
-  // All-zero input: publish g = 1.  Other workgroups may still read the
-  // sentinel or the 1.0, and both mean 1.
-  if (DYN && blockIdx.x == 0 && threadIdx.x == 0 && g == 1.0f)
-    *const_cast<float*>(ts) = 1.0f;
+                                                       float* ts, int nparts) {
+  float g;
+  if constexpr (DYN) {
+    // The amax launch's partial values, from this workgroup's own piece of q
+    // (nparts <= kPieceFloats = 2 floats per thread).  block_max's barrier
+    // orders these reads before any thread of the workgroup overwrites the
+    // piece with codes.
+    __shared__ float wave_max[kThreads / 64];
+    const float* part = reinterpret_cast<const float*>(q) + (int64_t)blockIdx.x * kPieceFloats;
+    const int t = threadIdx.x;
+    float m = 0.0f;
+    if (t < nparts) m = part[t];
+    if (t + kThreads < nparts) m = fmaxf(m, part[t + kThreads]);
+    const float mx = block_max(m, wave_max);
+    g = mx > 0.0f ? mx : 1.0f;  // all-zero matrix: g = 1
+    if (blockIdx.x == 0 && t == 0) *ts = g;
+  } else {
+    g = *ts;
+  }
   const float six_g = 6.0f * g;
   const I nb = (I)(k / 16);
   const I total = (I)rows * nb;
@@ -172,23 +186,28 @@ hipError_t launch_dt(const void* x, int64_t rows, int64_t k, int64_t ld_x, uint8
                      float* ts, int dynamic, hipStream_t stream) {
   const int64_t total = rows * (k / 16);
   const int64_t want = (total + kThreads - 1) / kThreads;
-  const int grid = (int)(want < 65536 ? (want > 0 ? want : 1) : 65536);
   if (dynamic) {
     if (total > 0) {
-      // One atomic per workgroup on a single word: size the amax grid so each
-      // thread covers kAmaxBlocks blocks per pass, at most 1024 workgroups.
-      const int64_t awant = (want + kAmaxBlocks - 1) / kAmaxBlocks;
-      const int agrid = (int)(awant < 1024 ? awant : 1024);
-      hipLaunchKernelGGL(k_amax_reset, dim3(1), dim3(64), 0, stream, ts);
-      hipLaunchKernelGGL((k_amax<DT, I>), dim3(agrid), dim3(kThreads), 0, stream, x, rows, k, ld_x, ts);
-      hipLaunchKernelGGL((k_quantize<DT, true, I>), dim3(grid), dim3(kThreads), 0, stream, x, rows,
-                         k, ld_x, q, sf, (const float*)ts);
+      // Quantise workgroups: one whole 256-block piece each in the first pass
+      // (the rest of the blocks follow in grid-stride passes), at most
+      // kMaxPieces.  Amax workgroups: each thread covers kAmaxBlocks blocks
+      // per pass, at most kMaxPartials; a matrix below one piece takes one.
+      int64_t pieces = total / kPiece;
+      if (pieces > kMaxPieces) pieces = kMaxPieces;
+      int64_t parts = (want + kAmaxBlocks - 1) / kAmaxBlocks;
+      if (parts > kMaxPartials) parts = kMaxPartials;
+      if (pieces < 1) pieces = parts = 1;
+      hipLaunchKernelGGL((k_amax<DT, I>), dim3((unsigned)parts), dim3(kThreads), 0, stream, x, rows,
+                         k, ld_x, reinterpret_cast<float*>(q), (int)pieces);
+      hipLaunchKernelGGL((k_quantize<DT, true, I>), dim3((unsigned)pieces), dim3(kThreads), 0,
+                         stream, x, rows, k, ld_x, q, sf, ts, (int)parts);
     } else {
       hipLaunchKernelGGL(k_set_one, dim3(1), dim3(64), 0, stream, ts);
     }
   } else if (total > 0) {
+    const int grid = (int)(want < 65536 ? want : 65536);
     hipLaunchKernelGGL((k_quantize<DT, false, I>), dim3(grid), dim3(kThreads), 0, stream, x, rows,
-                       k, ld_x, q, sf, (const float*)ts);
+                       k, ld_x, q, sf, ts, 0);
   }
   return hipGetLastError();
 }
@@ -199,7 +218,7 @@ template <int DT>
 hipError_t launch_idx(const void* x, int64_t rows, int64_t k, int64_t ld_x, uint8_t* q, uint8_t* sf,
                       float* ts, int dynamic, hipStream_t stream) {
   const int64_t total = rows * (k / 16);
-  const int64_t reach = total + (int64_t)kAmaxBlocks * 1024 * kThreads + 65536LL * kThreads;
+  const int64_t reach = total + (int64_t)kAmaxBlocks * kMaxPartials * kThreads + 65536LL * kThreads;
   if (reach < INT32_MAX) return launch_dt<DT, int32_t>(x, rows, k, ld_x, q, sf, ts, dynamic, stream);
   return launch_dt<DT, int64_t>(x, rows, k, ld_x, q, sf, ts, dynamic, stream);
 }

@@ -138,3 +138,35 @@ def test_deterministic_and_stream_safe():
         q2, sf2, g2 = moe_fp4.quantize(x)
     s.synchronize()
     assert torch.equal(q1, q2) and torch.equal(sf1, sf2) and torch.equal(g1, g2)
+
+
+# Dynamic scale: the amax launch hands its per-workgroup values to the quantise
+# launch inside q itself, one 2 KB piece (256 blocks) per quantise workgroup, with
+# at most 2048 pieces and 512 partial values.  These sizes sit on either side of
+# one piece, of the piece limit and of the partial limit, with the matrix's
+# largest element in its last block, which the grid-stride passes after the
+# first piece reach.
+@pytest.mark.parametrize("rows,k", [(1, 4080), (1, 4096), (1, 4112), (2, 4096),
+                                    (1024, 8192), (1025, 8192), (4099, 6144)])
+def test_dynamic_scale_piece_boundaries(rows, k):
+    rng = np.random.default_rng(rows * 7 + k)
+    x = gen.bf16_round(rng.standard_normal((rows, k)).astype(np.float32))
+    x[-1, -1] = np.float32(-57.5)
+    _check(x, torch.bfloat16, label="piece boundaries, amax in the last block")
+
+
+def test_dynamic_scale_ignores_what_q_held_before():
+    """q is the hand-over space between the two launches: whatever it held before
+    the call (here the codes of a matrix with a larger amax) must not leak into g."""
+    from block_scaled_fp4_05_amd import moe_fp4
+    big = dev(gen.bf16_round(gen.normal((64, 4096), 8) * np.float32(1000.0))).to(torch.bfloat16)
+    small = gen.bf16_round(gen.normal((64, 4096), 9))
+    say("quantize dynamic into a reused q buffer")
+    q, sf, g = moe_fp4.quantize(big)
+    ts = torch.full((1,), 7.0, dtype=torch.float32, device="cuda")
+    xt = dev(small).to(torch.bfloat16)
+    moe_fp4.quantize(xt, ts, q=q, sf=sf, dynamic=True)
+    torch.cuda.synchronize()
+    oq, osf, og = orc.quantize(small)
+    assert np.float32(ts.cpu().numpy()[0]).view(np.uint32) == np.float32(og).view(np.uint32)
+    assert np.array_equal(q.cpu().numpy(), oq) and np.array_equal(sf.cpu().numpy(), osf)
