@@ -25,6 +25,12 @@ constexpr int32_t kMaxExperts = 8192;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Whether the byte ranges [p, p + pb) and [q, q + qb) share a byte.
+bool overlap(const void* p, int64_t pb, const void* q, int64_t qb) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  return pb > 0 && qb > 0 && a < b + (uintptr_t)qb && b < a + (uintptr_t)pb;
+}
+
 int check_gemm_shape(int32_t num_experts, int64_t m_total, int64_t n, int64_t k) {
   if (num_experts < 1 || m_total < 0 || n < 1 || k < 1) return MOE_FP4_ERR_SHAPE;
   if (num_experts > kMaxExperts) return MOE_FP4_ERR_UNSUPPORTED;
@@ -84,6 +90,16 @@ int moe_fp4_quantize(const void* x, int in_dtype, int64_t rows, int64_t k, int64
   if (rows > 0 && (!aligned(x, 16) || (ld_x * esize) % 16 != 0 || !aligned(q, 8)))
     return MOE_FP4_ERR_ALIGN;
   if (rows > 0 && (rows > INT64_MAX / k)) return MOE_FP4_ERR_SHAPE;
+  // The four buffers must be distinct: the dynamic mode hands the amax pass's
+  // partial values to the quantise pass inside q while x is still being read,
+  // and writes the tensor scale while q is being read.
+  if (rows > 0) {
+    const int64_t xb = ((rows - 1) * ld_x + k) * esize, qb = rows * (k / 2), sb = rows * (k / 16);
+    if (overlap(x, xb, q, qb) || overlap(x, xb, sf, sb) || overlap(x, xb, tensor_scale, 4) ||
+        overlap(q, qb, sf, sb) || overlap(q, qb, tensor_scale, 4) ||
+        overlap(sf, sb, tensor_scale, 4))
+      return MOE_FP4_ERR_ARG;
+  }
   hipError_t err = moe_fp4::launch_quantize(x, in_dtype, rows, k, ld_x, q, sf, tensor_scale,
                                             scale_mode == MOE_FP4_SCALE_DYNAMIC ? 1 : 0,
                                             reinterpret_cast<hipStream_t>(stream));
@@ -217,11 +233,6 @@ int grouped_gemm_finalize(const uint8_t* a_q, const uint8_t* a_sf, const float* 
   hipError_t err =
       moe_fp4::launch_grouped_gemm_finalize(p, t, reinterpret_cast<hipStream_t>(stream));
   return err == hipSuccess ? MOE_FP4_OK : MOE_FP4_ERR_HIP;
-}
-
-bool overlap(const void* p, int64_t pb, const void* q, int64_t qb) {
-  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
-  return pb > 0 && qb > 0 && a < b + (uintptr_t)qb && b < a + (uintptr_t)pb;
 }
 
 int grouped_gemm_swiglu(const uint8_t* a_q, const uint8_t* a_sf, const float* a_scale,

@@ -99,8 +99,11 @@ enum {
  * Inputs must be finite; the result for NaN or Inf inputs is unspecified.
  * DYNAMIC mode also needs amax = 0 or fl(amax / 2688) > 0 (amax above about
  * 2^-138); below that g underflows to 0 and the block scales are undefined.
+ * x, q, sf and tensor_scale must not overlap (q also carries values between
+ * the two passes of the DYNAMIC mode).
  * Errors: NULL (x, q, sf or tensor_scale NULL with rows > 0; tensor_scale
- * NULL always), SHAPE (rows < 0, k <= 0, k % 16, ld_x < k), ALIGN, ARG, HIP.
+ * NULL always), SHAPE (rows < 0, k <= 0, k % 16, ld_x < k), ALIGN, ARG
+ * (unknown in_dtype or scale_mode; overlapping buffers), HIP.
  */
 int moe_fp4_quantize(const void* x, int in_dtype, int64_t rows, int64_t k, int64_t ld_x,
                      uint8_t* q, uint8_t* sf, float* tensor_scale, int scale_mode,

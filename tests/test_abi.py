@@ -95,7 +95,8 @@ P16 = 0x10000  # 16-byte aligned fake address
 
 
 def _q(**kw):
-    a = dict(x=P16, dt=0, rows=4, k=64, ld=64, q=P16, sf=P16, ts=P16, mode=1, stream=None)
+    a = dict(x=P16, dt=0, rows=4, k=64, ld=64, q=2 * P16, sf=3 * P16, ts=4 * P16, mode=1,
+             stream=None)
     a.update(kw)
     return _lib().quantize_raw(a["x"], a["dt"], a["rows"], a["k"], a["ld"], a["q"], a["sf"],
                                a["ts"], a["mode"], a["stream"])
@@ -107,6 +108,10 @@ def _q(**kw):
     (dict(sf=None), 1), (dict(rows=-1), 2), (dict(k=0), 2), (dict(k=24), 2), (dict(ld=32), 2),
     (dict(x=P16 + 8), 3), (dict(ld=68), 3), (dict(q=P16 + 4), 3), (dict(ts=P16 + 2), 3),
     (dict(dt=1, ld=66), 3), (dict(dt=1, ld=60), 2), (dict(dt=1, ld=65, k=48), 3),
+    # overlapping buffers (x spans 4 rows x 128 bytes, q 128 bytes, sf 16 bytes)
+    (dict(q=P16 + 504), 6), (dict(sf=P16 + 511), 6), (dict(ts=P16 + 508), 6),
+    (dict(sf=2 * P16 + 120), 6), (dict(ts=2 * P16 + 124), 6), (dict(ts=3 * P16 + 12), 6),
+    (dict(sf=P16, mode=0), 6),
 ])
 def test_quantize_rejects(kw, status):
     assert _q(**kw) == status
