@@ -469,18 +469,28 @@ def cpu_baseline(prob):
     w_scale = np.empty(E, np.float32)
     for e in range(E):
         w_q[e], w_sf[e], w_scale[e] = orc.quantize(prob.host_weights[e])
-    t0 = time.perf_counter()
-    a_q, a_sf, a_scale = orc.quantize(prob.x_host)
-    t1 = time.perf_counter()
-    R, ref = orc.grouped_gemm(a_q, a_sf, a_scale, w_q, w_sf, w_scale, prob.offsets,
-                              a_row_index=prob.row_token)
-    t2 = time.perf_counter()
-    secs = t2 - t0
+    # Whole steps, repeated until about 10 s of host time (at most 30 steps);
+    # the figures are means per step.
+    q_s = g_s = 0.0
+    passes = 0
+    while passes == 0 or (q_s + g_s < 10.0 and passes < 30):
+        t0 = time.perf_counter()
+        a_q, a_sf, a_scale = orc.quantize(prob.x_host)
+        t1 = time.perf_counter()
+        R, ref = orc.grouped_gemm(a_q, a_sf, a_scale, w_q, w_sf, w_scale, prob.offsets,
+                                  a_row_index=prob.row_token)
+        t2 = time.perf_counter()
+        q_s += t1 - t0
+        g_s += t2 - t1
+        passes += 1
+    secs = (q_s + g_s) / passes
     base = dict(value=round(prob.flops / secs / 1e12, 6), unit="TFLOPS", cores=orc.num_threads(),
                 kind="oracle",
                 sample=f"whole {w.name} step: quantise {w.tokens}x{k} activations + grouped GEMM "
-                       f"over all {prob.m_total} routed rows ({E} experts, N={n}, K={k}), once",
-                seconds=round(secs, 3), quantize_s=round(t1 - t0, 3), gemm_s=round(t2 - t1, 3))
+                       f"over all {prob.m_total} routed rows ({E} experts, N={n}, K={k}), "
+                       f"{passes} steps, mean per step",
+                seconds=round(secs, 3), quantize_s=round(q_s / passes, 3),
+                gemm_s=round(g_s / passes, 3), steps=passes)
     return base, R, ref
 
 
