@@ -29,18 +29,21 @@ LIB_PATH = os.environ.get("FP4_ORACLE_LIB") or os.path.join(_HERE, "liboracle_fp
 _lib = None
 
 
-def build(force: bool = False) -> str:
+def build(force: bool = False, src: str | None = None, out: str | None = None) -> str:
     """Compile the oracle with gcc (-O2, OpenMP, no FP contraction).
 
     FP4_ORACLE_LIB may name another build of the same source (used to check, on
-    the CPU, that the pins fail on a deliberately broken copy)."""
-    if force or not os.path.exists(LIB_PATH):
-        tmp = LIB_PATH + ".tmp%d" % os.getpid()
+    the CPU, that the pins fail on a deliberately broken copy); `src` and `out`
+    compile such a copy."""
+    src = src or _SRC
+    out = out or LIB_PATH
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
-               "-Wall", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"]
+               "-Wall", "-shared", "-fPIC", src, "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
-        os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+        os.replace(tmp, out)
+    return out
 
 
 def _load():
