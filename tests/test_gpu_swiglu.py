@@ -181,11 +181,18 @@ CASES = [(32, 8, 2, 64, 256), (48, 6, 3, 80, 512), (64, 4, 2, 128, 2048), (100, 
 @pytest.mark.parametrize("case", range(len(CASES)))
 def test_swiglu_matches_oracle(case, packed, exact):
     T, E, topk, inter, k = CASES[case]
-    if packed and inter % 64:
-        pytest.skip("packed weights need I % 64 == 0")
     P = _problem(T, E, topk, inter, k, 900 + 10 * case, exact=exact)
     R, S = _oracle_parts(P)
     g2 = _calibrated(R)
+    if packed and inter % 64:
+        # A packed 64-row group would straddle the gate and up halves: the host
+        # rejects the call (UNSUPPORTED) before anything is launched.
+        from block_scaled_fp4_05_amd import moe_fp4
+        say(f"swiglu T={T} E={E} I={inter} packed: expect UNSUPPORTED")
+        with pytest.raises(moe_fp4.MoeFp4Error) as err:
+            _gpu_swiglu(P, g2, packed=True)
+        assert err.value.status == moe_fp4.ERR_UNSUPPORTED
+        return
     say(f"swiglu T={T} E={E} top{topk} I={inter} k={k} packed={packed} exact={exact} g={g2:.4g}")
     q, sf = _gpu_swiglu(P, g2, packed=packed)
     _check(q, sf, R, S, g2, k, f"case {case}", exact=exact)
