@@ -69,6 +69,10 @@ def parse_args():
     ap.add_argument("--finalize", action="store_true",
                     help="also time the finalize GEMM (routing-weighted sum into token order) "
                          "against the plain GEMM plus a separate weighted combine")
+    ap.add_argument("--layer", action="store_true",
+                    help="also time a whole MoE FFN layer on this shard: quantise, gate+up GEMM "
+                         "with the SwiGLU + NVFP4 epilogue, down-projection GEMM, token-order "
+                         "combine (the workload's weights are the gate+up projection)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a device copy of known size (counter scale factor)")
     return ap.parse_args()
@@ -395,6 +399,152 @@ def swiglu_report(prob, steps):
     return res
 
 
+def layer_report(prob, steps):
+    """One whole Mixture-of-Experts FFN layer on this shard, from the library's entry
+    points (the chain the layer test checks against the oracle):
+      1. moe_fp4_quantize       the step's BF16 tokens -> NVFP4 (dynamic scale);
+      2. moe_grouped_gemm_fp4_swiglu  gate+up (this workload's weights, the first N/2
+                                rows the gate; tensor scales divided by sqrt(K) so the
+                                pre-activations are O(1)) -> the NVFP4 intermediate
+                                h [m_total][N/2] at a static scale calibrated once;
+      3. moe_grouped_gemm_fp4   down projection: h (routed rows, in order) times seeded
+                                N(0,1) weights [E][K][N/2] -> BF16 rows [m_total][K];
+      4. moe_fp4_combine        routing-weighted sum of each token's rows -> BF16 tokens.
+    Both weight sets are packed and rotated over device copies like the workload's."""
+    import numpy as np
+    import torch
+    from block_scaled_fp4_05_amd import moe_fp4
+    from workloads import gen
+    w = prob.w
+    if w.n % 64:
+        raise SystemExit("--layer needs N a multiple of 64 (N = 2I, I a multiple of 32)")
+    inter, hidden, E = w.n // 2, w.k, w.experts
+    dev = torch.device("cuda")
+    scaled = [(q, sf, (sc / w.k ** 0.5).contiguous()) for q, sf, sc in prob.weights]
+    # Down-projection weights [E][hidden][inter], seeded N(0,1), quantised on the GPU.
+    w2_q = torch.empty((E, hidden, inter // 2), dtype=torch.uint8, device=dev)
+    w2_sf = torch.empty((E, hidden, inter // 16), dtype=torch.uint8, device=dev)
+    w2_scale = torch.empty(E, dtype=torch.float32, device=dev)
+    for e in range(E):
+        we = torch.from_numpy(gen.expert_weight(e, hidden, inter, 400 + w.index)).to(dev)
+        moe_fp4.quantize(we, tensor_scale=w2_scale[e:e + 1], q=w2_q[e], sf=w2_sf[e], dynamic=True)
+    w2_scale /= inter ** 0.5
+    if prob.packed:
+        w2_q = moe_fp4.pack_weights(w2_q)
+    down = [(w2_q, w2_sf, w2_scale)] + [(w2_q.clone(), w2_sf.clone(), w2_scale.clone())
+                                        for _ in range(len(prob.weights) - 1)]
+    h_scale = torch.empty(1, dtype=torch.float32, device=dev)
+    h_q = torch.empty((prob.m_total, inter // 2), dtype=torch.uint8, device=dev)
+    h_sf = torch.empty((prob.m_total, inter // 16), dtype=torch.uint8, device=dev)
+    rows = torch.empty((prob.m_total, hidden), dtype=torch.bfloat16, device=dev)
+    # Token -> routed rows (a token's rows in row order) and seeded routing weights.
+    row_token = prob.row_token.astype(np.int64)
+    order = np.argsort(row_token, kind="stable")
+    counts = np.bincount(row_token, minlength=w.tokens)
+    starts = np.concatenate([[0], np.cumsum(counts)[:-1]])
+    tr_host = np.full((w.tokens, w.topk), -1, np.int32)
+    tr_host[row_token[order], np.arange(len(order)) - np.repeat(starts, counts)] = order
+    weight = np.random.default_rng(800 + w.index).uniform(0.0, 1.0, prob.m_total)
+    wt_host = np.where(tr_host >= 0, weight[np.maximum(tr_host, 0)], 0.0).astype(np.float32)
+    token_rows = torch.from_numpy(tr_host).to(dev)
+    token_weights = torch.from_numpy(wt_host).to(dev)
+    out = torch.empty((w.tokens, hidden), dtype=torch.bfloat16, device=dev)
+
+    def quant(i):
+        moe_fp4.quantize(prob.x, tensor_scale=prob.g, q=prob.q, sf=prob.sf, dynamic=True)
+
+    def gate_up(i):
+        q13, sf13, s13 = scaled[i % len(scaled)]
+        moe_fp4.grouped_gemm_swiglu(prob.q, prob.sf, prob.g, q13, sf13, s13, prob.off, h_scale,
+                                    a_row_index=prob.idx, h_q=h_q, h_sf=h_sf,
+                                    m_total=prob.m_total, packed=prob.packed)
+
+    def down_proj(i):
+        q2, sf2, s2 = down[i % len(down)]
+        moe_fp4.grouped_gemm(h_q, h_sf, h_scale, q2, sf2, s2, prob.off, out=rows,
+                             m_total=prob.m_total, packed=prob.packed)
+
+    def comb(i):
+        moe_fp4.combine(rows, token_rows, token_weights, out=out)
+
+    def layer(i):
+        quant(i)
+        gate_up(i)
+        down_proj(i)
+        comb(i)
+
+    # Static intermediate scale: amax of one unfused gate+up activation / 2688.
+    quant(0)
+    q13, sf13, s13 = scaled[0]
+    moe_fp4.grouped_gemm(prob.q, prob.sf, prob.g, q13, sf13, s13, prob.off, a_row_index=prob.idx,
+                         out=prob.out, m_total=prob.m_total, packed=prob.packed)
+    y = prob.out.float()
+    h_scale.copy_((torch.nn.functional.silu(y[:, :inter]) * y[:, inter:]).abs().max().reshape(1)
+                  / 2688.0)
+
+    def timed(fn):
+        warm(fn)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(steps):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps * 1e3
+
+    res = dict(tokens=w.tokens, experts=E, topk=w.topk, hidden=hidden, inter=inter,
+               layer_us=round(timed(layer), 2), quantize_us=round(timed(quant), 2),
+               gate_up_swiglu_us=round(timed(gate_up), 2), down_us=round(timed(down_proj), 2),
+               combine_us=round(timed(comb), 2))
+    # The same chain replayed from a HIP graph (one layer per weight copy in one
+    # capture), which leaves only the GPU's own gaps between the launches.  Every
+    # replay is checked against the eager result, bit for bit, with eager work and
+    # synchronisations in between.
+    ncopy = len(scaled)
+    layer(ncopy - 1)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(ncopy):
+            layer(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        for i in range(ncopy):
+            layer(i)
+    replays_ok = True
+    for _ in range(3):
+        out.zero_()
+        layer(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        replays_ok = replays_ok and bool(torch.equal(out, eager))
+    if not replays_ok:
+        raise SystemExit("layer graph replay differs from the eager layer")
+    reps = max(1, steps // ncopy)
+    warm(lambda i: graph.replay())
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        graph.replay()
+    b.record()
+    torch.cuda.synchronize()
+    res["layer_graph_us"] = round(a.elapsed_time(b) / (reps * ncopy) * 1e3, 2)
+    res["graph_replays_match_eager"] = replays_ok
+    flops = 2.0 * prob.m_total * (w.n * hidden + hidden * inter)
+    res["layer_tflops"] = round(flops / (res["layer_us"] * 1e-6) / 1e12, 2)
+    res["tokens_per_s"] = round(w.tokens / (res["layer_us"] * 1e-6), 1)
+    nz = int(np.count_nonzero(np.diff(prob.offsets)))
+    wbytes = nz * (w.n * hidden + hidden * inter) * (0.5 + 1.0 / 16.0)
+    res["weight_bytes"] = int(wbytes)
+    res["weight_stream_gbps"] = round(wbytes / (res["layer_us"] * 1e-6) / 1e9, 1)
+    return res
+
+
 def plan_of(prob):
     from block_scaled_fp4_05_amd import moe_fp4
     w = prob.w
@@ -557,6 +707,9 @@ def main():
     if args.swiglu:
         swi = swiglu_report(prob, args.steps)
         log("swiglu " + json.dumps(swi))
+    if args.layer:
+        lay = layer_report(prob, args.steps)
+        log("layer " + json.dumps(lay))
 
     secondary = None
     if args.secondary and args.secondary != "none" and args.secondary != args.workload:
@@ -603,6 +756,8 @@ def main():
         line["finalize"] = fin
     if args.swiglu:
         line["swiglu"] = swi
+    if args.layer:
+        line["layer"] = lay
     print(json.dumps(line), flush=True)
 
 
