@@ -1,10 +1,12 @@
-"""GPU parity of moe_grouped_gemm_fp4 at the largest sizes the library accepts.
+"""GPU parity of moe_grouped_gemm_fp4 and moe_fp4_combine at the largest sizes the
+library accepts.
 
 The header's limits: at most 8192 experts; n * k/2 and a_rows * k/2 below
 2^31 - 4096 (every byte offset into one expert's weights and into the
-activations is a 32-bit buffer offset); ldo at most 2^23.  Each case sits at
-its limit, the oracle computing sampled rows and columns (the bar of the other
-GEMM tests: per-row relative L2 error <= 2e-3 on the sampled columns)."""
+activations is a 32-bit buffer offset); ldo at most 2^23; each combine buffer
+below 2^31 - 4096 bytes.  Each case sits at its limit, the oracle computing
+sampled rows and columns (the bar of the other GEMM tests: per-row relative L2
+error <= 2e-3 on the sampled columns; the combine's FP32 sums against FP64)."""
 import numpy as np
 import pytest
 import torch
@@ -144,3 +146,39 @@ def test_byte_offsets_at_the_32_bit_limit():
     out = _gemm(a_q, a_sf, args[2], packed, w_sf, args[5], args[6], m, row_index=dev(picks),
                 packed=True)
     _check(bf16_bits_of(out)[:, cols], R, ref, "32-bit byte offsets, packed")
+
+
+def test_combine_buffers_at_the_32_bit_limit():
+    """moe_fp4_combine with its routed-row buffer and its FP32 output each just below
+    2^31 - 4096 bytes: tokens near both ends, and a skipped slot, checked in FP64."""
+    from block_scaled_fp4_05_amd import moe_fp4
+    n = 16384
+    m = (LIMIT - 1) // (2 * n)            # 65535 BF16 rows of 32 KB
+    T = (LIMIT - 1) // (4 * n)            # 32767 FP32 token rows of 64 KB
+    assert m * n * 2 < LIMIT and (m + 1) * n * 2 >= LIMIT
+    assert T * n * 4 < LIMIT and (T + 1) * n * 4 >= LIMIT
+    say(f"limits: combine rows {m}x{n} bf16, out {T}x{n} fp32")
+    gen_t = torch.Generator(device="cuda").manual_seed(4242)
+    rows = torch.randn((m, n), generator=gen_t, device="cuda").to(torch.bfloat16)
+    topk = 2
+    tr = torch.arange(T * topk, dtype=torch.int32, device="cuda").reshape(T, topk)
+    tr[T - 1, 1] = -1                     # a skipped slot
+    tr[T - 2, 0] = m - 1                  # the last routed row
+    tw = torch.rand((T, topk), generator=gen_t, device="cuda")
+    out = moe_fp4.combine(rows, tr, tw, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    picks = np.unique(np.concatenate([[0, 1, T - 2, T - 1], rng.choice(T, 12, replace=False)]))
+    tr_h, tw_h = tr.cpu().numpy(), tw.cpu().numpy().astype(np.float64)
+    for t in picks:
+        ref = np.zeros(n)
+        mag = np.zeros(n)
+        for s in range(topk):
+            r = int(tr_h[t, s])
+            if 0 <= r < m:
+                v = rows[r].float().cpu().numpy().astype(np.float64)
+                ref += tw_h[t, s] * v
+                mag += abs(tw_h[t, s] * v)
+        got = out[int(t)].cpu().numpy().astype(np.float64)
+        # FP32 sums of two exactly representable products: within 2 ulps of the terms.
+        assert np.all(np.abs(got - ref) <= 2.0 ** -22 * mag + 1e-30), f"token {t}"
