@@ -1,7 +1,7 @@
 """GPU parity of moe_grouped_gemm_fp4 and moe_fp4_combine at the largest sizes the
 library accepts.
 
-The header's limits: at most 8192 experts; n * k/2 and a_rows * k/2 below
+The header's limits: at most 8192 experts; m_total below 2^29 - 1024; n * k/2 and a_rows * k/2 below
 2^31 - 4096 (every byte offset into one expert's weights and into the
 activations is a 32-bit buffer offset); ldo at most 2^23; each combine buffer
 below 2^31 - 4096 bytes.  Each case sits at its limit, the oracle computing
@@ -182,3 +182,31 @@ def test_combine_buffers_at_the_32_bit_limit():
         got = out[int(t)].cpu().numpy().astype(np.float64)
         # FP32 sums of two exactly representable products: within 2 ulps of the terms.
         assert np.all(np.abs(got - ref) <= 2.0 ** -22 * mag + 1e-30), f"token {t}"
+
+
+def test_most_routed_rows():
+    """m_total = 2^29 - 1025, the largest the header accepts (the row index's byte
+    offsets then approach 2^31): two experts, 4 distinct token rows gathered by the
+    row index, 16 output columns; sampled rows near both ends checked."""
+    E, n, k, a_rows = 2, 16, 256, 4
+    m = 2 ** 29 - 1025
+    split = 1000
+    off = np.array([0, split, m], np.int32)
+    a_q = gen.random_fp4_bytes((a_rows, k // 2), 61)
+    a_sf = gen.random_e4m3_codes((a_rows, k // 16), 62, 0x30, 0x40)
+    w_q = gen.random_fp4_bytes((E, n, k // 2), 63)
+    w_sf = gen.random_e4m3_codes((E, n, k // 16), 64, 0x30, 0x40)
+    w_scale = np.array([0.5, 2.0], np.float32)
+    a_scale = np.float32(1.0)
+    say(f"limits: m_total={m} (row index {4 * m / 2**30:.2f} GiB, output {2 * m * n / 2**30:.1f} GiB)")
+    idx = (torch.arange(m, dtype=torch.int64, device="cuda") * 7 % a_rows).to(torch.int32)
+    out = _gemm(dev(a_q), dev(a_sf), dev(np.array([a_scale])), dev(w_q), dev(w_sf), dev(w_scale),
+                dev(off), m, row_index=idx)
+    rng = np.random.default_rng(7)
+    sel = np.unique(np.concatenate([[0, split - 1, split, m - 2, m - 1],
+                                    rng.integers(0, m, 24)])).astype(np.int64)
+    idx_sel = idx[torch.from_numpy(sel).to("cuda")].cpu().numpy()
+    sel_off = np.array([0, int(np.sum(sel < split)), len(sel)], np.int32)
+    R, ref = orc.grouped_gemm(a_q, a_sf, a_scale, w_q, w_sf, w_scale, sel_off, a_row_index=idx_sel)
+    _check(bf16_bits_of(out[torch.from_numpy(sel).to("cuda")]), R, ref, "m_total at its limit")
+    del out, idx
