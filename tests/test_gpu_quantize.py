@@ -146,13 +146,16 @@ def test_deterministic_and_stream_safe():
 # one piece, of the piece limit and of the partial limit, with the matrix's
 # largest element in its last block, which the grid-stride passes after the
 # first piece reach.
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("rows,k", [(1, 4080), (1, 4096), (1, 4112), (2, 4096),
                                     (1024, 8192), (1025, 8192), (4099, 6144)])
-def test_dynamic_scale_piece_boundaries(rows, k):
+def test_dynamic_scale_piece_boundaries(rows, k, dtype):
     rng = np.random.default_rng(rows * 7 + k)
-    x = gen.bf16_round(rng.standard_normal((rows, k)).astype(np.float32))
+    x = rng.standard_normal((rows, k)).astype(np.float32)
+    if dtype == torch.bfloat16:
+        x = gen.bf16_round(x)
     x[-1, -1] = np.float32(-57.5)
-    _check(x, torch.bfloat16, label="piece boundaries, amax in the last block")
+    _check(x, dtype, label="piece boundaries, amax in the last block")
 
 
 def test_dynamic_scale_ignores_what_q_held_before():
