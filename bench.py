@@ -22,6 +22,9 @@ kernel alone on the launch stream (rocprofv3's per-kernel average measures
 the same thing).
 
   python bench.py [--steps K] [--warmup W] [--workload c3] [--secondary c4]
+  python bench.py --swiglu     # + gate+up GEMM with the SwiGLU + NVFP4 epilogue vs unfused
+  python bench.py --finalize   # + finalize: fused atomics vs plain GEMM + token-order combine
+  python bench.py --layer      # + a whole MoE FFN layer (eager and from a HIP graph)
   python bench.py --copy-calibration   # a plain copy of known size, for counter scaling
 """
 from __future__ import annotations
