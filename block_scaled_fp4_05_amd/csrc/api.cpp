@@ -90,6 +90,8 @@ int moe_fp4_quantize(const void* x, int in_dtype, int64_t rows, int64_t k, int64
   if (rows > 0 && (!aligned(x, 16) || (ld_x * esize) % 16 != 0 || !aligned(q, 8)))
     return MOE_FP4_ERR_ALIGN;
   if (rows > 0 && (rows > INT64_MAX / k)) return MOE_FP4_ERR_SHAPE;
+  // x's extent, ((rows - 1) * ld_x + k) * esize bytes, must be representable.
+  if (rows > 1 && (ld_x > (INT64_MAX / esize - k) / (rows - 1))) return MOE_FP4_ERR_SHAPE;
   // The four buffers must be distinct: the dynamic mode hands the amax pass's
   // partial values to the quantise pass inside q while x is still being read,
   // and writes the tensor scale while q is being read.

@@ -102,7 +102,8 @@ enum {
  * x, q, sf and tensor_scale must not overlap (q also carries values between
  * the two passes of the DYNAMIC mode).
  * Errors: NULL (x, q, sf or tensor_scale NULL with rows > 0; tensor_scale
- * NULL always), SHAPE (rows < 0, k <= 0, k % 16, ld_x < k), ALIGN, ARG
+ * NULL always), SHAPE (rows < 0, k <= 0, k % 16, ld_x < k, or x's extent
+ * not representable in 64 bits), ALIGN, ARG
  * (unknown in_dtype or scale_mode; overlapping buffers), HIP.
  */
 int moe_fp4_quantize(const void* x, int in_dtype, int64_t rows, int64_t k, int64_t ld_x,

@@ -112,6 +112,8 @@ def _q(**kw):
     (dict(q=P16 + 504), 6), (dict(sf=P16 + 511), 6), (dict(ts=P16 + 508), 6),
     (dict(sf=2 * P16 + 120), 6), (dict(ts=2 * P16 + 124), 6), (dict(ts=3 * P16 + 12), 6),
     (dict(sf=P16, mode=0), 6),
+    # an input extent beyond int64
+    (dict(rows=1 << 20, ld=1 << 50), 2),
 ])
 def test_quantize_rejects(kw, status):
     assert _q(**kw) == status
