@@ -38,7 +38,7 @@ int check_gemm_shape(int32_t num_experts, int64_t m_total, int64_t n, int64_t k)
   // Row-index entries are addressed with 32-bit byte offsets.
   if (n > INT32_MAX / 2 || m_total > INT32_MAX / 4 - 1024) return MOE_FP4_ERR_UNSUPPORTED;
   // One expert's packed weights are addressed with 32-bit buffer offsets.
-  if (n * (k / 2) > (int64_t)INT32_MAX - 4096) return MOE_FP4_ERR_UNSUPPORTED;
+  if (k / 2 > ((int64_t)INT32_MAX - 4096) / n) return MOE_FP4_ERR_UNSUPPORTED;
   // The work-list counts items in int32: bound the largest possible count.
   const int64_t max_mtiles = m_total / 16 + (m_total < num_experts ? m_total : num_experts);
   const int64_t n_tiles = (n + 31) / 32;
@@ -145,7 +145,7 @@ int grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const float* a_scale, 
     return MOE_FP4_ERR_ALIGN;
   // Activations and one item's output rows are addressed with 32-bit buffer
   // offsets as well.
-  if (a_rows * (k / 2) > (int64_t)INT32_MAX - 4096 || ldo > (1 << 23))
+  if (a_rows > ((int64_t)INT32_MAX - 4096) / (k / 2) || ldo > (1 << 23))
     return MOE_FP4_ERR_UNSUPPORTED;
   const GemmTile t = moe_fp4::choose_tile(num_experts, m_total, n, k, getenv("MOE_FP4_TILE"));
   // Packed weights fix the per-wavefront K step to the layout's granule.
@@ -197,9 +197,9 @@ int grouped_gemm_finalize(const uint8_t* a_q, const uint8_t* a_sf, const float* 
       !aligned(expert_offsets, 4) || (a_row_index && !aligned(a_row_index, 4)) ||
       !aligned(out_token, 4) || !aligned(row_weight, 4))
     return MOE_FP4_ERR_ALIGN;
-  if (a_rows * (k / 2) > (int64_t)INT32_MAX - 4096) return MOE_FP4_ERR_UNSUPPORTED;
+  if (a_rows > ((int64_t)INT32_MAX - 4096) / (k / 2)) return MOE_FP4_ERR_UNSUPPORTED;
   // The token rows are addressed with 32-bit byte offsets.
-  if (num_tokens > (int64_t)INT32_MAX / 4 || num_tokens * ldo * 4 > (int64_t)INT32_MAX - 4096)
+  if (num_tokens > (int64_t)INT32_MAX / 4 || ldo > ((int64_t)INT32_MAX - 4096) / 4 / num_tokens)
     return MOE_FP4_ERR_UNSUPPORTED;
   GemmTile t = moe_fp4::choose_tile(num_experts, m_total, n, k, getenv("MOE_FP4_TILE"));
   // The finalize epilogue runs in the per-wave kernel with 64-column items;
@@ -257,7 +257,7 @@ int grouped_gemm_swiglu(const uint8_t* a_q, const uint8_t* a_sf, const float* a_
       !aligned(h_scale, 4) || !aligned(expert_offsets, 4) ||
       (a_row_index && !aligned(a_row_index, 4)))
     return MOE_FP4_ERR_ALIGN;
-  if (a_rows * (k / 2) > (int64_t)INT32_MAX - 4096) return MOE_FP4_ERR_UNSUPPORTED;
+  if (a_rows > ((int64_t)INT32_MAX - 4096) / (k / 2)) return MOE_FP4_ERR_UNSUPPORTED;
   // The intermediate has n/2 columns in whole 16-element blocks; packed weights
   // are read in whole 64-row groups, which must not straddle the gate/up halves.
   if (n % 32 != 0 || (w_packed && (n / 2) % 64 != 0)) return MOE_FP4_ERR_UNSUPPORTED;
@@ -306,7 +306,7 @@ int repack(const uint8_t* src, uint8_t* dst, int32_t num_experts, int64_t n, int
   if (!src || !dst) return MOE_FP4_ERR_NULL;
   if (num_experts < 1 || n < 1 || k < 1) return MOE_FP4_ERR_SHAPE;
   if (n % 16 != 0 || k % moe_fp4::kKStep != 0) return MOE_FP4_ERR_UNSUPPORTED;
-  if (n > INT32_MAX / 2 || n * (k / 2) > (int64_t)INT32_MAX - 4096) return MOE_FP4_ERR_UNSUPPORTED;
+  if (n > INT32_MAX / 2 || k / 2 > ((int64_t)INT32_MAX - 4096) / n) return MOE_FP4_ERR_UNSUPPORTED;
   if (!aligned(src, 16) || !aligned(dst, 16)) return MOE_FP4_ERR_ALIGN;
   const uintptr_t bytes = (uintptr_t)num_experts * (uintptr_t)n * (uintptr_t)(k / 2);
   const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);

@@ -137,6 +137,8 @@ def _g(**kw):
     (dict(n=24, ldo=24), 4), (dict(k=128), 4), (dict(k=320), 4), (dict(E=20000), 4), (dict(E=8193), 4),
     (dict(a_q=P16 + 8), 3), (dict(w_sf=P16 + 4), 3), (dict(out=P16 + 8), 3), (dict(ldo=68), 3),
     (dict(off=P16 + 2), 3), (dict(idx=P16 + 2), 3), (dict(a_scale=P16 + 1), 3),
+    # sizes whose products would not fit in 64 bits are refused, not overflowed
+    (dict(k=1 << 60), 4), (dict(a_rows=1 << 62), 4), (dict(a_rows=1 << 62, idx=P16), 4),
 ])
 def test_gemm_rejects(kw, status):
     assert _g(**kw) == status
@@ -223,7 +225,7 @@ def _gf(**kw):
     (dict(tok=None), 1), (dict(wt=None), 1), (dict(out=None), 1), (dict(w_q=None), 1),
     (dict(pk=2), 6), (dict(T=0), 2), (dict(ldo=32), 2), (dict(E=0), 2), (dict(n=24, ldo=24), 4),
     (dict(k=320), 4), (dict(out=P16 + 2), 3), (dict(tok=P16 + 2), 3), (dict(wt=P16 + 1), 3),
-    (dict(T=1 << 24, ldo=64), 4),
+    (dict(T=1 << 24, ldo=64), 4), (dict(ldo=1 << 61), 4), (dict(a_rows=1 << 62), 4),
 ])
 def test_finalize_rejects(kw, status):
     assert _gf(**kw) == status
