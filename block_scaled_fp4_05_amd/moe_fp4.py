@@ -110,6 +110,58 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+class _AtLeast(int):
+    """A shape entry that admits any extent of at least this value."""
+
+    def __repr__(self):
+        return f">={int(self)}"
+
+
+def _need(t, name, dtype, shape=None, contiguous=True, rows=False):
+    """Check a tensor argument before its pointer is handed to the library: its dtype,
+    its shape (None entries are free, _AtLeast(x) entries admit x or more), and its
+    layout: contiguous, or with rows=True only unit stride along the last axis (rows
+    at any leading dimension).  Raises ValueError.  (Plain loops: it runs on every
+    call of a decode step.)"""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: expected a tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if shape is not None:
+        ts = t.shape
+        ok = len(ts) == len(shape)
+        if ok:
+            for i in range(len(shape)):
+                w = shape[i]
+                if w is not None and ((ts[i] < w) if type(w) is _AtLeast else (ts[i] != w)):
+                    ok = False
+                    break
+        if not ok:
+            raise ValueError(f"{name}: shape {tuple(ts)}, expected {tuple(shape)}")
+    if rows:
+        if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+            raise ValueError(f"{name}: rows must have unit column stride")
+    elif contiguous and not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _same_cuda(names, *tensors):
+    """All given tensors (None skipped) are CUDA tensors on one device; `names` lists
+    them, space-separated, for the error message."""
+    dev = -1
+    for t in tensors:
+        if t is None:
+            continue
+        d = t.get_device()
+        if d < 0 or (dev >= 0 and d != dev):
+            devs = {nm: str(x.device) for nm, x in zip(names.split(), tensors) if x is not None}
+            if d < 0:
+                bad = [nm for nm, v in devs.items() if not v.startswith("cuda")]
+                raise ValueError(f"{bad[0]}: must be a CUDA tensor (got {devs[bad[0]]})")
+            raise ValueError(f"tensors on several devices: {devs}")
+        dev = d
+
+
 def quantize_raw(x_ptr, in_dtype, rows, k, ld_x, q_ptr, sf_ptr, scale_ptr, scale_mode, stream_ptr):
     """Direct call with raw pointers; returns the status code."""
     return lib().moe_fp4_quantize(x_ptr, in_dtype, rows, k, ld_x, q_ptr, sf_ptr, scale_ptr,
@@ -129,9 +181,12 @@ def gemm_packed_raw(*args):
 def pack_weights(w_q: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Row-major weight codes [E][n][k/2] (uint8, CUDA) -> the packed layout the
     packed GEMM reads (same shape and size; a byte permutation)."""
+    _need(w_q, "w_q", torch.uint8, (None, None, None))
     E, n, kb = w_q.shape
     if out is None:
         out = torch.empty_like(w_q)
+    _need(out, "out", torch.uint8, (E, n, kb))
+    _same_cuda("w_q out", w_q, out)
     st = lib().moe_fp4_pack_weights(_ptr(w_q), _ptr(out), E, n, 2 * kb, _stream(stream))
     if st != OK:
         raise MoeFp4Error(st, "moe_fp4_pack_weights")
@@ -140,9 +195,12 @@ def pack_weights(w_q: torch.Tensor, out: torch.Tensor | None = None, stream=None
 
 def unpack_weights(w_packed: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Inverse of pack_weights."""
+    _need(w_packed, "w_packed", torch.uint8, (None, None, None))
     E, n, kb = w_packed.shape
     if out is None:
         out = torch.empty_like(w_packed)
+    _need(out, "out", torch.uint8, (E, n, kb))
+    _same_cuda("w_packed out", w_packed, out)
     st = lib().moe_fp4_unpack_weights(_ptr(w_packed), _ptr(out), E, n, 2 * kb, _stream(stream))
     if st != OK:
         raise MoeFp4Error(st, "moe_fp4_unpack_weights")
@@ -179,11 +237,34 @@ def quantize(x: torch.Tensor, tensor_scale: torch.Tensor | None = None, q=None, 
         if not dynamic:
             raise ValueError("a static quantisation needs tensor_scale")
         tensor_scale = torch.empty(1, dtype=torch.float32, device=dev)
+    _need(q, "q", torch.uint8, (_AtLeast(rows), k // 2))
+    _need(sf, "sf", torch.uint8, (_AtLeast(rows), k // 16))
+    _need(tensor_scale, "tensor_scale", torch.float32, (_AtLeast(1),))
+    _same_cuda("x q sf tensor_scale", x, q, sf, tensor_scale)
     st = lib().moe_fp4_quantize(_ptr(x), dt, rows, k, x.stride(0), _ptr(q), _ptr(sf),
                                 _ptr(tensor_scale), mode, _stream(stream))
     if st != OK:
         raise MoeFp4Error(st, "moe_fp4_quantize")
     return q, sf, tensor_scale
+
+
+def _gemm_operands(a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets, a_row_index, m_total):
+    """Check the operands shared by the grouped-GEMM entry points; returns
+    (E, n, k, a_rows, m_total)."""
+    _need(w_q, "w_q", torch.uint8, (None, None, None))
+    E, n, kb = w_q.shape
+    _need(a_q, "a_q", torch.uint8, (None, kb))
+    a_rows = a_q.shape[0]
+    _need(a_sf, "a_sf", torch.uint8, (a_rows, kb // 8))
+    _need(a_scale, "a_scale", torch.float32, (_AtLeast(1),))
+    _need(w_sf, "w_sf", torch.uint8, (E, n, kb // 8))
+    _need(w_scale, "w_scale", torch.float32, (E,))
+    _need(offsets, "offsets", torch.int32, (E + 1,))
+    if m_total is None:
+        m_total = a_row_index.shape[0] if a_row_index is not None else a_rows
+    if a_row_index is not None:
+        _need(a_row_index, "a_row_index", torch.int32, (m_total,))
+    return E, n, 2 * kb, a_rows, m_total
 
 
 def grouped_gemm(a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets, a_row_index=None, out=None,
@@ -193,13 +274,12 @@ def grouped_gemm(a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets, a_row_index=No
     a_row_index int32 [m_total] or None.  m_total defaults to a_row_index's length,
     else a_rows.  packed: w_q is in the packed layout (pack_weights).  Returns out,
     a BF16 tensor [m_total][n] (or the given `out`)."""
-    E, n, kb = w_q.shape
-    k = 2 * kb
-    a_rows = a_q.shape[0]
-    if m_total is None:
-        m_total = a_row_index.shape[0] if a_row_index is not None else a_rows
+    E, n, k, a_rows, m_total = _gemm_operands(a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets,
+                                              a_row_index, m_total)
     if out is None:
         out = torch.empty((m_total, n), dtype=torch.bfloat16, device=w_q.device)
+    _need(out, "out", torch.bfloat16, (_AtLeast(m_total), _AtLeast(n)), rows=True)
+    _same_cuda("a_q a_sf a_scale w_q w_sf w_scale offsets a_row_index out", a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets, a_row_index, out)
     fn = lib().moe_grouped_gemm_fp4_packed if packed else lib().moe_grouped_gemm_fp4
     st = fn(_ptr(a_q), _ptr(a_sf), _ptr(a_scale), a_rows, _ptr(a_row_index), _ptr(w_q), _ptr(w_sf),
             _ptr(w_scale), _ptr(offsets), E, m_total, n, k, _ptr(out), out.stride(0), _stream(stream))
@@ -219,11 +299,12 @@ def grouped_gemm_finalize(a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets, out_t
     """Grouped GEMM with the finalize epilogue: routed row r adds row_weight[r] times its
     result into row out_token[r] of `out` (float32 CUDA tensor [num_tokens][ldo],
     accumulated into).  Other arguments as grouped_gemm.  Returns out."""
-    E, n, kb = w_q.shape
-    k = 2 * kb
-    a_rows = a_q.shape[0]
-    if m_total is None:
-        m_total = a_row_index.shape[0] if a_row_index is not None else a_rows
+    E, n, k, a_rows, m_total = _gemm_operands(a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets,
+                                              a_row_index, m_total)
+    _need(out_token, "out_token", torch.int32, (m_total,))
+    _need(row_weight, "row_weight", torch.float32, (m_total,))
+    _need(out, "out", torch.float32, (None, _AtLeast(n)), rows=True)
+    _same_cuda("a_q a_sf a_scale w_q w_sf w_scale offsets a_row_index out_token row_weight out", a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets, a_row_index, out_token, row_weight, out)
     st = lib().moe_grouped_gemm_fp4_finalize(
         _ptr(a_q), _ptr(a_sf), _ptr(a_scale), a_rows, _ptr(a_row_index), _ptr(w_q), _ptr(w_sf),
         _ptr(w_scale), 1 if packed else 0, _ptr(offsets), E, m_total, n, k, _ptr(out_token),
@@ -246,16 +327,17 @@ def grouped_gemm_swiglu(a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets, h_scale
     intermediate's static tensor scale.  Other arguments as grouped_gemm.  Returns
     (h_q uint8 [m_total][I/2], h_sf uint8 [m_total][I/16]), the down projection's
     activations (or the given buffers)."""
-    E, n, kb = w_q.shape
-    k = 2 * kb
-    a_rows = a_q.shape[0]
-    if m_total is None:
-        m_total = a_row_index.shape[0] if a_row_index is not None else a_rows
+    E, n, k, a_rows, m_total = _gemm_operands(a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets,
+                                              a_row_index, m_total)
     dev = w_q.device
     if h_q is None:
         h_q = torch.empty((m_total, n // 4), dtype=torch.uint8, device=dev)
     if h_sf is None:
         h_sf = torch.empty((m_total, n // 32), dtype=torch.uint8, device=dev)
+    _need(h_scale, "h_scale", torch.float32, (_AtLeast(1),))
+    _need(h_q, "h_q", torch.uint8, (_AtLeast(m_total), n // 4))
+    _need(h_sf, "h_sf", torch.uint8, (_AtLeast(m_total), n // 32))
+    _same_cuda("a_q a_sf a_scale w_q w_sf w_scale offsets a_row_index h_scale h_q h_sf", a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets, a_row_index, h_scale, h_q, h_sf)
     st = lib().moe_grouped_gemm_fp4_swiglu(
         _ptr(a_q), _ptr(a_sf), _ptr(a_scale), a_rows, _ptr(a_row_index), _ptr(w_q), _ptr(w_sf),
         _ptr(w_scale), 1 if packed else 0, _ptr(offsets), E, m_total, n, k, _ptr(h_scale),
@@ -276,10 +358,19 @@ def combine(rows, token_rows, token_weights, out=None, residual=None, out_dtype=
     in FP32, slots in order.  rows: BF16 CUDA tensor [m_total][>= n] (the grouped GEMM's
     output); token_rows int32 / token_weights float32 [num_tokens][topk].  Returns out
     ([num_tokens][n] of out_dtype, bfloat16 or float32)."""
+    _need(rows, "rows", torch.bfloat16, (None, None), rows=True)
     m_total, n = rows.shape
+    _need(token_rows, "token_rows", torch.int32, (None, None))
     T, topk = token_rows.shape
+    _need(token_weights, "token_weights", torch.float32, (T, topk))
+    if residual is not None:
+        _need(residual, "residual", torch.float32, (T, _AtLeast(n)), rows=True)
     if out is None:
         out = torch.empty((T, n), dtype=out_dtype, device=rows.device)
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"out: dtype {out.dtype}, expected bfloat16 or float32")
+    _need(out, "out", out.dtype, (T, _AtLeast(n)), rows=True)
+    _same_cuda("rows token_rows token_weights residual out", rows, token_rows, token_weights, residual, out)
     dt = OUT_FP32 if out.dtype == torch.float32 else OUT_BF16
     st = lib().moe_fp4_combine(_ptr(rows), rows.stride(0), m_total, _ptr(token_rows),
                                _ptr(token_weights), topk, T, n, _ptr(residual),
