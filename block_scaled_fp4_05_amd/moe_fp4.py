@@ -104,9 +104,13 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream):
+def _stream(stream, dev):
+    """The launch stream (default: the current stream of the current device), which
+    must belong to the tensors' device `dev`: the kernels run on the stream's device."""
     if stream is None:
         stream = torch.cuda.current_stream()
+    if stream.device_index != dev:
+        raise ValueError(f"stream on cuda:{stream.device_index}, tensors on cuda:{dev}")
     return ctypes.c_void_p(stream.cuda_stream)
 
 
@@ -146,8 +150,8 @@ def _need(t, name, dtype, shape=None, contiguous=True, rows=False):
 
 
 def _same_cuda(names, *tensors):
-    """All given tensors (None skipped) are CUDA tensors on one device; `names` lists
-    them, space-separated, for the error message."""
+    """All given tensors (None skipped) are CUDA tensors on one device, which is
+    returned; `names` lists them, space-separated, for the error message."""
     dev = -1
     for t in tensors:
         if t is None:
@@ -160,6 +164,7 @@ def _same_cuda(names, *tensors):
                 raise ValueError(f"{bad[0]}: must be a CUDA tensor (got {devs[bad[0]]})")
             raise ValueError(f"tensors on several devices: {devs}")
         dev = d
+    return dev
 
 
 def quantize_raw(x_ptr, in_dtype, rows, k, ld_x, q_ptr, sf_ptr, scale_ptr, scale_mode, stream_ptr):
@@ -186,8 +191,8 @@ def pack_weights(w_q: torch.Tensor, out: torch.Tensor | None = None, stream=None
     if out is None:
         out = torch.empty_like(w_q)
     _need(out, "out", torch.uint8, (E, n, kb))
-    _same_cuda("w_q out", w_q, out)
-    st = lib().moe_fp4_pack_weights(_ptr(w_q), _ptr(out), E, n, 2 * kb, _stream(stream))
+    dev = _same_cuda("w_q out", w_q, out)
+    st = lib().moe_fp4_pack_weights(_ptr(w_q), _ptr(out), E, n, 2 * kb, _stream(stream, dev))
     if st != OK:
         raise MoeFp4Error(st, "moe_fp4_pack_weights")
     return out
@@ -200,8 +205,8 @@ def unpack_weights(w_packed: torch.Tensor, out: torch.Tensor | None = None, stre
     if out is None:
         out = torch.empty_like(w_packed)
     _need(out, "out", torch.uint8, (E, n, kb))
-    _same_cuda("w_packed out", w_packed, out)
-    st = lib().moe_fp4_unpack_weights(_ptr(w_packed), _ptr(out), E, n, 2 * kb, _stream(stream))
+    dev = _same_cuda("w_packed out", w_packed, out)
+    st = lib().moe_fp4_unpack_weights(_ptr(w_packed), _ptr(out), E, n, 2 * kb, _stream(stream, dev))
     if st != OK:
         raise MoeFp4Error(st, "moe_fp4_unpack_weights")
     return out
@@ -240,9 +245,9 @@ def quantize(x: torch.Tensor, tensor_scale: torch.Tensor | None = None, q=None, 
     _need(q, "q", torch.uint8, (_AtLeast(rows), k // 2))
     _need(sf, "sf", torch.uint8, (_AtLeast(rows), k // 16))
     _need(tensor_scale, "tensor_scale", torch.float32, (_AtLeast(1),))
-    _same_cuda("x q sf tensor_scale", x, q, sf, tensor_scale)
+    dev = _same_cuda("x q sf tensor_scale", x, q, sf, tensor_scale)
     st = lib().moe_fp4_quantize(_ptr(x), dt, rows, k, x.stride(0), _ptr(q), _ptr(sf),
-                                _ptr(tensor_scale), mode, _stream(stream))
+                                _ptr(tensor_scale), mode, _stream(stream, dev))
     if st != OK:
         raise MoeFp4Error(st, "moe_fp4_quantize")
     return q, sf, tensor_scale
@@ -279,10 +284,10 @@ def grouped_gemm(a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets, a_row_index=No
     if out is None:
         out = torch.empty((m_total, n), dtype=torch.bfloat16, device=w_q.device)
     _need(out, "out", torch.bfloat16, (_AtLeast(m_total), _AtLeast(n)), rows=True)
-    _same_cuda("a_q a_sf a_scale w_q w_sf w_scale offsets a_row_index out", a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets, a_row_index, out)
+    dev = _same_cuda("a_q a_sf a_scale w_q w_sf w_scale offsets a_row_index out", a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets, a_row_index, out)
     fn = lib().moe_grouped_gemm_fp4_packed if packed else lib().moe_grouped_gemm_fp4
     st = fn(_ptr(a_q), _ptr(a_sf), _ptr(a_scale), a_rows, _ptr(a_row_index), _ptr(w_q), _ptr(w_sf),
-            _ptr(w_scale), _ptr(offsets), E, m_total, n, k, _ptr(out), out.stride(0), _stream(stream))
+            _ptr(w_scale), _ptr(offsets), E, m_total, n, k, _ptr(out), out.stride(0), _stream(stream, dev))
     if st != OK:
         raise MoeFp4Error(st, "moe_grouped_gemm_fp4_packed" if packed else "moe_grouped_gemm_fp4")
     return out
@@ -304,11 +309,11 @@ def grouped_gemm_finalize(a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets, out_t
     _need(out_token, "out_token", torch.int32, (m_total,))
     _need(row_weight, "row_weight", torch.float32, (m_total,))
     _need(out, "out", torch.float32, (None, _AtLeast(n)), rows=True)
-    _same_cuda("a_q a_sf a_scale w_q w_sf w_scale offsets a_row_index out_token row_weight out", a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets, a_row_index, out_token, row_weight, out)
+    dev = _same_cuda("a_q a_sf a_scale w_q w_sf w_scale offsets a_row_index out_token row_weight out", a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets, a_row_index, out_token, row_weight, out)
     st = lib().moe_grouped_gemm_fp4_finalize(
         _ptr(a_q), _ptr(a_sf), _ptr(a_scale), a_rows, _ptr(a_row_index), _ptr(w_q), _ptr(w_sf),
         _ptr(w_scale), 1 if packed else 0, _ptr(offsets), E, m_total, n, k, _ptr(out_token),
-        _ptr(row_weight), _ptr(out), out.stride(0), out.shape[0], _stream(stream))
+        _ptr(row_weight), _ptr(out), out.stride(0), out.shape[0], _stream(stream, dev))
     if st != OK:
         raise MoeFp4Error(st, "moe_grouped_gemm_fp4_finalize")
     return out
@@ -337,11 +342,11 @@ def grouped_gemm_swiglu(a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets, h_scale
     _need(h_scale, "h_scale", torch.float32, (_AtLeast(1),))
     _need(h_q, "h_q", torch.uint8, (_AtLeast(m_total), n // 4))
     _need(h_sf, "h_sf", torch.uint8, (_AtLeast(m_total), n // 32))
-    _same_cuda("a_q a_sf a_scale w_q w_sf w_scale offsets a_row_index h_scale h_q h_sf", a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets, a_row_index, h_scale, h_q, h_sf)
+    dev = _same_cuda("a_q a_sf a_scale w_q w_sf w_scale offsets a_row_index h_scale h_q h_sf", a_q, a_sf, a_scale, w_q, w_sf, w_scale, offsets, a_row_index, h_scale, h_q, h_sf)
     st = lib().moe_grouped_gemm_fp4_swiglu(
         _ptr(a_q), _ptr(a_sf), _ptr(a_scale), a_rows, _ptr(a_row_index), _ptr(w_q), _ptr(w_sf),
         _ptr(w_scale), 1 if packed else 0, _ptr(offsets), E, m_total, n, k, _ptr(h_scale),
-        _ptr(h_q), _ptr(h_sf), _stream(stream))
+        _ptr(h_q), _ptr(h_sf), _stream(stream, dev))
     if st != OK:
         raise MoeFp4Error(st, "moe_grouped_gemm_fp4_swiglu")
     return h_q, h_sf
@@ -370,12 +375,12 @@ def combine(rows, token_rows, token_weights, out=None, residual=None, out_dtype=
     if out.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError(f"out: dtype {out.dtype}, expected bfloat16 or float32")
     _need(out, "out", out.dtype, (T, _AtLeast(n)), rows=True)
-    _same_cuda("rows token_rows token_weights residual out", rows, token_rows, token_weights, residual, out)
+    dev = _same_cuda("rows token_rows token_weights residual out", rows, token_rows, token_weights, residual, out)
     dt = OUT_FP32 if out.dtype == torch.float32 else OUT_BF16
     st = lib().moe_fp4_combine(_ptr(rows), rows.stride(0), m_total, _ptr(token_rows),
                                _ptr(token_weights), topk, T, n, _ptr(residual),
                                residual.stride(0) if residual is not None else 0, _ptr(out), dt,
-                               out.stride(0), _stream(stream))
+                               out.stride(0), _stream(stream, dev))
     if st != OK:
         raise MoeFp4Error(st, "moe_fp4_combine")
     return out

@@ -72,3 +72,12 @@ def test_swiglu_finalize_combine_and_pack_check_their_tensors():
         moe_fp4.pack_weights(torch.zeros(2, 64, 128, dtype=U8), out=torch.zeros(2, 64, 64, dtype=U8))
     with pytest.raises(ValueError, match="must be a CUDA tensor"):
         moe_fp4.unpack_weights(torch.zeros(2, 64, 128, dtype=U8))
+
+
+def test_the_launch_stream_must_be_on_the_tensors_device():
+    class FakeStream:
+        device_index, cuda_stream = 1, 0
+
+    with pytest.raises(ValueError, match="stream on cuda:1, tensors on cuda:0"):
+        moe_fp4._stream(FakeStream(), 0)
+    assert moe_fp4._stream(FakeStream(), 1).value is None
