@@ -68,11 +68,9 @@ __global__ void k_set_one(float* ts) {
   if (blockIdx.x == 0 && threadIdx.x == 0) *ts = 1.0f;
 }
 
-// Blocks (k_amax) or 16-byte chunks (k_amax_flat) per thread per iteration of
-// the amax pass: all their loads are in flight before the reduction.  Both
-// cover 128 bytes of BF16 input.
+// Blocks per thread per iteration of the amax pass: all their loads are in
+// flight before the reduction.
 constexpr int kAmaxBlocks = 4;
-constexpr int kAmaxChunks = 8;
 // Blocks of one quantise workgroup's first pass, and the floats of q they
 // cover (8 bytes of codes per block): room for this many partial values.
 constexpr int kPiece = kThreads;
@@ -95,8 +93,8 @@ __device__ __forceinline__ float block_max(float m, float* wave_max) {
   return r;
 }
 
-// I: the index type (32-bit whenever every chunk and block index fits, which
-// avoids 64-bit division in the index arithmetic).  Workgroup p reduces its share of the
+// I: the index type (32-bit whenever rows * k/16 fits, which avoids 64-bit
+// division in the index arithmetic).  Workgroup p reduces its share of the
 // blocks to fl(amax / 2688) (0 if all its elements are 0) and stores it as
 // float p of each of the `pieces` 2 KB pieces at the start of q.
 template <int DT, typename I>
@@ -121,53 +119,6 @@ __global__ __launch_bounds__(kThreads) void k_amax(const void* x, int64_t rows, 
     for (int j = 0; j < kAmaxBlocks; ++j)
 #pragma unroll
       for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[j][i]));
-  }
-  const float wg = block_max(m, wave_max);
-  const float g = wg / 2688.0f;  // IEEE division, rounded to nearest even (0 stays 0)
-  for (int w = threadIdx.x; w < pieces; w += kThreads)
-    partials[(int64_t)w * kPieceFloats + blockIdx.x] = g;
-}
-
-// The same pass for matrices that reach the kMaxPartials cap.  The maximum
-// does not depend on the blocks, so it reads the matrix as 16-byte chunks,
-// consecutive lanes on consecutive chunks of a row: each load instruction of a
-// wave covers 1 KB of a row.  Measured against k_amax on BF16 input: 5% faster
-// at 4096 x 6144 and 3% at 8192 x 8192, but 0.6 us slower at 512 x 6144,
-// where every thread makes one pass.
-template <int DT, typename I>
-__global__ __launch_bounds__(kThreads) void k_amax_flat(const void* x, int64_t rows, int64_t k,
-                                                   int64_t ld_x, float* partials, int pieces) {
-  __shared__ float wave_max[kThreads / 64];
-  constexpr int kEsize = DT == 0 ? 2 : 4;
-  const I cpr = (I)(k * kEsize / 16);  // chunks per row
-  const I total = (I)rows * cpr;
-  const I stride = (I)gridDim.x * kThreads;
-  const uint8_t* const base = reinterpret_cast<const uint8_t*>(x);
-  float m = 0.0f;
-  for (I c = (I)blockIdx.x * kThreads + threadIdx.x; c < total; c += kAmaxChunks * stride) {
-    u32x4_t w[kAmaxChunks];
-#pragma unroll
-    for (int j = 0; j < kAmaxChunks; ++j) {
-      // Past the end, re-read the last chunk: a duplicate leaves the max as it is.
-      I cj = c + (I)j * stride;
-      cj = cj < total ? cj : total - 1;
-      const I row = cj / cpr;
-      w[j] = load_16B(base + (int64_t)row * ld_x * kEsize + (int64_t)(cj - row * cpr) * 16);
-    }
-#pragma unroll
-    for (int j = 0; j < kAmaxChunks; ++j) {
-      // Each lane to a scalar before the bit cast (see load_block16).
-      const uint32_t u[4] = {w[j][0], w[j][1], w[j][2], w[j][3]};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if constexpr (DT == 0) {  // two BF16 values, widened exactly
-          m = fmaxf(m, fabsf(__builtin_bit_cast(float, u[i] << 16)));
-          m = fmaxf(m, fabsf(__builtin_bit_cast(float, u[i] & 0xFFFF0000u)));
-        } else {
-          m = fmaxf(m, fabsf(__builtin_bit_cast(float, u[i])));
-        }
-      }
-    }
   }
   const float wg = block_max(m, wave_max);
   const float g = wg / 2688.0f;  // IEEE division, rounded to nearest even (0 stays 0)
@@ -240,20 +191,14 @@ hipError_t launch_dt(const void* x, int64_t rows, int64_t k, int64_t ld_x, uint8
       // Quantise workgroups: one whole 256-block piece each in the first pass
       // (the rest of the blocks follow in grid-stride passes), at most
       // kMaxPieces.  Amax workgroups: each thread covers kAmaxBlocks blocks
-      // per pass, at most kMaxPartials, past which the chunked pass takes
-      // over; a matrix below one piece takes one.
+      // per pass, at most kMaxPartials; a matrix below one piece takes one.
       int64_t pieces = total / kPiece;
       if (pieces > kMaxPieces) pieces = kMaxPieces;
       int64_t parts = (want + kAmaxBlocks - 1) / kAmaxBlocks;
-      const bool capped = parts > kMaxPartials;
-      if (capped) parts = kMaxPartials;
+      if (parts > kMaxPartials) parts = kMaxPartials;
       if (pieces < 1) pieces = parts = 1;
-      if (capped)
-        hipLaunchKernelGGL((k_amax_flat<DT, I>), dim3((unsigned)parts), dim3(kThreads), 0, stream, x,
-                           rows, k, ld_x, reinterpret_cast<float*>(q), (int)pieces);
-      else
-        hipLaunchKernelGGL((k_amax<DT, I>), dim3((unsigned)parts), dim3(kThreads), 0, stream, x,
-                           rows, k, ld_x, reinterpret_cast<float*>(q), (int)pieces);
+      hipLaunchKernelGGL((k_amax<DT, I>), dim3((unsigned)parts), dim3(kThreads), 0, stream, x, rows,
+                         k, ld_x, reinterpret_cast<float*>(q), (int)pieces);
       hipLaunchKernelGGL((k_quantize<DT, true, I>), dim3((unsigned)pieces), dim3(kThreads), 0,
                          stream, x, rows, k, ld_x, q, sf, ts, (int)parts);
     } else {
@@ -267,14 +212,13 @@ hipError_t launch_dt(const void* x, int64_t rows, int64_t k, int64_t ld_x, uint8
   return hipGetLastError();
 }
 
-// 32-bit indices when every chunk and block index (including one stride past
-// the last) fits, 64-bit otherwise.
+// 32-bit block indices when every index (including one stride past the last
+// block) fits, 64-bit otherwise.
 template <int DT>
 hipError_t launch_idx(const void* x, int64_t rows, int64_t k, int64_t ld_x, uint8_t* q, uint8_t* sf,
                       float* ts, int dynamic, hipStream_t stream) {
   const int64_t total = rows * (k / 16);
-  const int64_t reach = total * (DT == 0 ? 2 : 4) + (int64_t)kAmaxChunks * kMaxPartials * kThreads +
-                        65536LL * kThreads;
+  const int64_t reach = total + (int64_t)kAmaxBlocks * kMaxPartials * kThreads + 65536LL * kThreads;
   if (reach < INT32_MAX) return launch_dt<DT, int32_t>(x, rows, k, ld_x, q, sf, ts, dynamic, stream);
   return launch_dt<DT, int64_t>(x, rows, k, ld_x, q, sf, ts, dynamic, stream);
 }

@@ -173,24 +173,3 @@ def test_dynamic_scale_ignores_what_q_held_before():
     oq, osf, og = orc.quantize(small)
     assert np.float32(ts.cpu().numpy()[0]).view(np.uint32) == np.float32(og).view(np.uint32)
     assert np.array_equal(q.cpu().numpy(), oq) and np.array_equal(sf.cpu().numpy(), osf)
-
-
-# Once the amax grid reaches its 512-workgroup cap, the amax pass reads 16-byte
-# chunks (8 BF16 or 4 FP32 values), 8 per thread per pass: chunks c + j * stride,
-# j = 0..7, stride = 512 * 256 chunks, then the next pass.  The matrix's largest
-# element sits in the chunk that slot j of one thread reads (slot 11: the second
-# pass's fourth).
-@pytest.mark.parametrize("dtype,slot", [(torch.bfloat16, 0), (torch.bfloat16, 1),
-                                        (torch.bfloat16, 7), (torch.bfloat16, 11),
-                                        (torch.float32, 5)])
-def test_dynamic_scale_chunked_amax_slots(dtype, slot):
-    rows, k = 2048, 6144
-    per_chunk = 8 if dtype == torch.bfloat16 else 4
-    cpr = k // per_chunk
-    rng = np.random.default_rng(900 + slot)
-    x = rng.standard_normal((rows, k)).astype(np.float32)
-    if dtype == torch.bfloat16:
-        x = gen.bf16_round(x)
-    c = slot * 512 * 256 + 777
-    x[c // cpr, (c % cpr) * per_chunk + per_chunk - 1] = np.float32(-75.0)
-    _check(x, dtype, label=f"chunked amax, largest element in slot {slot}")
