@@ -173,3 +173,22 @@ def test_dynamic_scale_ignores_what_q_held_before():
     oq, osf, og = orc.quantize(small)
     assert np.float32(ts.cpu().numpy()[0]).view(np.uint32) == np.float32(og).view(np.uint32)
     assert np.array_equal(q.cpu().numpy(), oq) and np.array_equal(sf.cpu().numpy(), osf)
+
+
+# At the 512-workgroup cap each amax thread reads blocks blk + j * stride,
+# j = 0..3, stride = 512 * 256 blocks, in passes.  The matrix's largest element
+# sits in the block that slot j of one thread reads (slot 5: the second pass's
+# second).
+@pytest.mark.parametrize("dtype,slot", [(torch.bfloat16, 0), (torch.bfloat16, 1),
+                                        (torch.bfloat16, 3), (torch.bfloat16, 5),
+                                        (torch.float32, 2)])
+def test_dynamic_scale_capped_amax_slots(dtype, slot):
+    rows, k = 2048, 6144
+    nb = k // 16
+    rng = np.random.default_rng(900 + slot)
+    x = rng.standard_normal((rows, k)).astype(np.float32)
+    if dtype == torch.bfloat16:
+        x = gen.bf16_round(x)
+    b = slot * 512 * 256 + 777
+    x[b // nb, (b % nb) * 16 + 15] = np.float32(-75.0)
+    _check(x, dtype, label=f"capped amax, largest element in slot {slot}")
