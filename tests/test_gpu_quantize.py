@@ -192,3 +192,17 @@ def test_dynamic_scale_capped_amax_slots(dtype, slot):
     b = slot * 512 * 256 + 777
     x[b // nb, (b % nb) * 16 + 15] = np.float32(-75.0)
     _check(x, dtype, label=f"capped amax, largest element in slot {slot}")
+
+
+# A matrix whose amax pass would take fewer workgroups than CUs at 4 blocks per
+# thread takes 8 per thread in half as many: on 512 x 6144 (196,608 blocks) 96
+# workgroups, blocks blk + j * stride, j = 0..7, stride = 96 * 256 blocks.
+@pytest.mark.parametrize("slot", [0, 3, 7])
+def test_dynamic_scale_small_amax_slots(slot):
+    rows, k = 512, 6144
+    nb = k // 16
+    rng = np.random.default_rng(950 + slot)
+    x = gen.bf16_round(rng.standard_normal((rows, k)).astype(np.float32))
+    b = slot * 96 * 256 + 777
+    x[b // nb, (b % nb) * 16] = np.float32(80.0)
+    _check(x, torch.bfloat16, label=f"small-matrix amax, largest element in slot {slot}")
