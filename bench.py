@@ -172,7 +172,7 @@ class Problem:
     def _prepare_raw(self):
         """The timed loops call the C entry points directly with pointers prepared
         here, once: the checked wrappers validate every tensor on every call, which
-        costs host time comparable to the ~10 us quantiser.  One call through each
+        costs host time comparable to the ~8 us quantiser.  One call through each
         checked wrapper first validates exactly these arguments."""
         import ctypes
         import torch
