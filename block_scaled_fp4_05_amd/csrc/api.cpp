@@ -108,6 +108,13 @@ int moe_fp4_quantize(const void* x, int in_dtype, int64_t rows, int64_t k, int64
   return err == hipSuccess ? MOE_FP4_OK : MOE_FP4_ERR_HIP;
 }
 
+size_t moe_grouped_gemm_fp4_workspace_size(int32_t num_experts, int64_t m_total, int64_t n,
+                                           int64_t k) {
+  (void)num_experts, (void)m_total, (void)n, (void)k;
+  // Every kernel builds its work list in LDS from the device offsets.
+  return 0;
+}
+
 int moe_grouped_gemm_fp4_plan(int32_t num_experts, int64_t m_total, int64_t n, int64_t k,
                               moe_fp4_gemm_plan* plan) {
   if (!plan) return MOE_FP4_ERR_NULL;
@@ -147,11 +154,14 @@ int grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const float* a_scale, 
   // offsets as well.
   if (a_rows > ((int64_t)INT32_MAX - 4096) / (k / 2) || ldo > (1 << 23))
     return MOE_FP4_ERR_UNSUPPORTED;
-  const GemmTile t = moe_fp4::choose_tile(num_experts, m_total, n, k, getenv("MOE_FP4_TILE"));
+  const GemmTile t = moe_fp4::fit_output_range(
+      moe_fp4::choose_tile(num_experts, m_total, n, k, getenv("MOE_FP4_TILE")), k, ldo);
   // Packed weights fix the per-wavefront K step to the layout's granule.
   if (packed && !t.tiled &&
       (t.n_blocks != 4 || t.k_sub != moe_fp4::packed_granule(k) / moe_fp4::kKStep))
     return MOE_FP4_ERR_UNSUPPORTED;
+  moe_fp4::log_tile(packed ? "moe_grouped_gemm_fp4_packed" : "moe_grouped_gemm_fp4", num_experts,
+                    m_total, n, k, ldo, t);
   if (m_total == 0) return MOE_FP4_OK;
   GemmArgs p = {};
   p.a_q = a_q;
@@ -208,6 +218,7 @@ int grouped_gemm_finalize(const uint8_t* a_q, const uint8_t* a_sf, const float* 
   if (t.n_blocks != 4 || t.k_sub > 2) return MOE_FP4_ERR_UNSUPPORTED;
   if (w_packed && t.k_sub != moe_fp4::packed_granule(k) / moe_fp4::kKStep)
     return MOE_FP4_ERR_UNSUPPORTED;
+  moe_fp4::log_tile("moe_grouped_gemm_fp4_finalize", num_experts, m_total, n, k, ldo, t);
   if (m_total == 0) return MOE_FP4_OK;
   GemmArgs p = {};
   p.a_q = a_q;
@@ -275,6 +286,7 @@ int grouped_gemm_swiglu(const uint8_t* a_q, const uint8_t* a_sf, const float* a_
   if (t.n_blocks != 4 || t.k_sub > 2) return MOE_FP4_ERR_UNSUPPORTED;
   if (w_packed && t.k_sub != moe_fp4::packed_granule(k) / moe_fp4::kKStep)
     return MOE_FP4_ERR_UNSUPPORTED;
+  moe_fp4::log_tile("moe_grouped_gemm_fp4_swiglu", num_experts, m_total, n, k, n, t);
   if (m_total == 0) return MOE_FP4_OK;
   GemmArgs p = {};
   p.a_q = a_q;

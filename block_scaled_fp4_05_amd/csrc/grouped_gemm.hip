@@ -4,8 +4,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <stdio.h>
+#include <stdlib.h>
+
 #include <map>
 #include <mutex>
+#include <string>
 #include <tuple>
 
 #include "grouped_gemm_kernel.h"
@@ -102,6 +106,40 @@ GemmTile choose_tile(int32_t num_experts, int64_t m_total, int64_t n, int64_t k,
     }
   }
   return t;
+}
+
+int32_t item_rows(const GemmTile& t) {
+  if (t.tiled >= 2) return 256;
+  if (t.tiled) return 128;
+  return 16 * t.m_blocks;
+}
+
+GemmTile fit_output_range(const GemmTile& t, int64_t k, int64_t ldo) {
+  if (!t.tiled || (int64_t)item_rows(t) * ldo * 2 <= (int64_t)INT32_MAX - 4096) return t;
+  return GemmTile{4, 4, 4, k % 512 == 0 ? 2 : 1, k % kSpan == 0 ? 1 : 0, 0};
+}
+
+void log_tile(const char* entry, int32_t num_experts, int64_t m_total, int64_t n, int64_t k,
+              int64_t ldo, const GemmTile& t) {
+  const char* env = getenv("MOE_FP4_LOG");
+  if (!env || !*env || (env[0] == '0' && env[1] == '\0')) return;
+  static std::mutex mu;
+  static std::string last;
+  char line[320];
+  const char* kind = t.tiled == 3 ? "256x256 workgroup tile for every expert"
+                     : t.tiled == 2 ? "256x256 workgroup tile for experts of >= 96 rows, "
+                                      "16x64 per-wave items for the rest"
+                     : t.tiled == 1 ? "128x128 workgroup tile" : "per-wave items";
+  snprintf(line, sizeof line,
+           "moe_fp4: %s E=%d m_total=%lld n=%lld k=%lld ldo=%lld: %s (tile %dx%d, k step %d, "
+           "weight scales %s)\n",
+           entry, (int)num_experts, (long long)m_total, (long long)n, (long long)k, (long long)ldo,
+           kind, item_rows(t), t.tiled >= 2 ? 256 : t.tiled ? 128 : 16 * t.n_blocks,
+           t.tiled ? 64 : 256 * t.k_sub, t.tiled ? "in LDS stages" : t.lds_scales ? "via LDS lines" : "in registers");
+  std::lock_guard<std::mutex> g(mu);
+  if (last == line) return;
+  last = line;
+  fputs(line, stderr);
 }
 
 int64_t gemm_lds_bytes(const GemmTile& t, int32_t num_experts) {

@@ -282,16 +282,19 @@ void k_grouped_gemm_big(const GemmArgs p) {
         }
       }
       __syncthreads();
-      const int32_t ldo = (int32_t)p.ldo;
+      // The host picks this tile only when 256 rows of ldo BF16 values stay
+      // below 2^31 - 4096 bytes, so the resource size and every offset fit 31 bits.
+      const uint32_t ldo = (uint32_t)p.ldo;
       const rsrc_t o = make_rsrc(p.out + (int64_t)it.row0 * ldo,
-                                 (uint32_t)((int64_t)it.rows_valid * ldo * 2));
+                                 (uint32_t)it.rows_valid * ldo * 2u);
       const int chunk = tid & 31, r0 = tid >> 5;  // 16 rows per pass of the workgroup
       const bool col_ok = it.n0 + 8 * chunk < n;
 #pragma unroll
       for (int i = 0; i < kBM / 16; ++i) {
         const int row = r0 + 16 * i;
         const u32x4_t d = *reinterpret_cast<const u32x4_t*>(tile + row * kTileRow + 16 * (chunk ^ (row & 31)));
-        const uint32_t off = col_ok ? (uint32_t)((row * ldo + it.n0 + 8 * chunk) * 2) : kOutOfRange;
+        const uint32_t off =
+            col_ok ? ((uint32_t)row * ldo + (uint32_t)(it.n0 + 8 * chunk)) * 2u : kOutOfRange;
         __builtin_amdgcn_raw_buffer_store_b128(d, o, off, 0, 0);
       }
       // The next item's first stage rewrites these buffers.

@@ -220,9 +220,11 @@ __global__ __launch_bounds__(kThreads) void k_grouped_gemm_tiled(const GemmArgs 
     // rows past the expert's end are dropped; column blocks past n are skipped.
     {
       typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-      const int32_t ldo = (int32_t)p.ldo;
+      // The host picks this tile only when 128 rows of ldo BF16 values stay
+      // below 2^31 - 4096 bytes, so the resource size and every offset fit 31 bits.
+      const uint32_t ldo = (uint32_t)p.ldo;
       const rsrc_t o = make_rsrc(p.out + (int64_t)it.row0 * ldo,
-                                 (uint32_t)((int64_t)it.rows_valid * ldo * 2));
+                                 (uint32_t)it.rows_valid * ldo * 2u);
 #pragma unroll
       for (int jb = 0; jb < 4; ++jb) {
         const int32_t col = it.n0 + 64 * wn + 16 * jb;
@@ -232,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void k_grouped_gemm_tiled(const GemmArgs 
             const float4_t v = acc[jb][ib];
             const bf16x4_t bv = {(__bf16)(v[0] * it.alpha), (__bf16)(v[1] * it.alpha),
                                  (__bf16)(v[2] * it.alpha), (__bf16)(v[3] * it.alpha)};
-            const uint32_t off = (uint32_t)(((64 * wm + 16 * ib + c) * ldo + col + 4 * g) * 2);
+            const uint32_t off = ((uint32_t)(64 * wm + 16 * ib + c) * ldo + (uint32_t)(col + 4 * g)) * 2u;
             __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, bv), o, off, 0, 0);
           }
         }

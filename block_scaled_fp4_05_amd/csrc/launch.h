@@ -67,6 +67,20 @@ GemmTile choose_tile(int32_t num_experts, int64_t m_total, int64_t n, int64_t k,
 // LDS bytes a workgroup of the grouped GEMM uses for `num_experts` experts.
 int64_t gemm_lds_bytes(const GemmTile& t, int32_t num_experts);
 
+// The tile `t`, or the per-wave tile of 64-row items when t is a workgroup
+// tile whose output rows (128 or 256 of them, ldo BF16 values apart) would not
+// fit one store resource: every kernel addresses one item's output rows with
+// 32-bit buffer offsets below 2^31 - 4096 bytes.
+GemmTile fit_output_range(const GemmTile& t, int64_t k, int64_t ldo);
+
+// Rows of output one item of tile t covers.
+int32_t item_rows(const GemmTile& t);
+
+// With MOE_FP4_LOG set (to anything but "0"), print the tile an entry point
+// chose to stderr, once per change of entry point, sizes or tile.
+void log_tile(const char* entry, int32_t num_experts, int64_t m_total, int64_t n, int64_t k,
+              int64_t ldo, const GemmTile& t);
+
 struct GemmArgs {
   const uint8_t* a_q;
   const uint8_t* a_sf;

@@ -28,6 +28,7 @@
 // (2 or 4) + 0.5625 bytes per element.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "fp4_device.h"
 #include "launch.h"
@@ -227,13 +228,18 @@ hipError_t launch_dt(const void* x, int64_t rows, int64_t k, int64_t ld_x, uint8
 }
 
 // 32-bit block indices when every index (including one stride past the last
-// block) fits, 64-bit otherwise.
+// block) fits, 64-bit otherwise.  MOE_FP4_INDEX64=1 takes the 64-bit build at
+// any size: the two builds must give the same bits, and only this switch lets a
+// test run the 64-bit one on a matrix that fits in memory many times over.
 template <int DT>
 hipError_t launch_idx(const void* x, int64_t rows, int64_t k, int64_t ld_x, uint8_t* q, uint8_t* sf,
                       float* ts, int dynamic, hipStream_t stream) {
   const int64_t total = rows * (k / 16);
   const int64_t reach = total + (int64_t)kAmaxBlocksSmall * kMaxPartials * kThreads + 65536LL * kThreads;
-  if (reach < INT32_MAX) return launch_dt<DT, int32_t>(x, rows, k, ld_x, q, sf, ts, dynamic, stream);
+  const char* force = getenv("MOE_FP4_INDEX64");
+  const bool wide = force && force[0] == '1' && force[1] == '\0';
+  if (reach < INT32_MAX && !wide)
+    return launch_dt<DT, int32_t>(x, rows, k, ld_x, q, sf, ts, dynamic, stream);
   return launch_dt<DT, int64_t>(x, rows, k, ld_x, q, sf, ts, dynamic, stream);
 }
 

@@ -12,7 +12,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmoe_fp4.so")
+# MOE_FP4_LIB may name another build of the same sources (the host-sanitizer
+# build of the CPU tests); by default the in-tree library.
+LIB_PATH = os.environ.get("MOE_FP4_LIB") or os.path.join(_PKG, "libmoe_fp4.so")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_HIP, ERR_ARG = range(7)
 OUT_BF16, OUT_FP32 = 0, 1
@@ -23,7 +25,8 @@ SCALE_STATIC, SCALE_DYNAMIC = 0, 1
 EXPORTED = ("moe_fp4_quantize", "moe_grouped_gemm_fp4", "moe_grouped_gemm_fp4_packed",
             "moe_grouped_gemm_fp4_finalize", "moe_grouped_gemm_fp4_swiglu", "moe_fp4_combine",
             "moe_fp4_pack_weights", "moe_fp4_unpack_weights", "moe_grouped_gemm_fp4_plan",
-            "moe_fp4_stage_bytes", "moe_fp4_status_string", "moe_fp4_abi_version")
+            "moe_grouped_gemm_fp4_workspace_size", "moe_fp4_stage_bytes",
+            "moe_fp4_status_string", "moe_fp4_abi_version")
 
 
 class MoeFp4Error(RuntimeError):
@@ -70,6 +73,8 @@ def lib() -> ctypes.CDLL:
         f.restype = i
     L.moe_grouped_gemm_fp4_plan.argtypes = [i32, i64, i64, i64, ctypes.POINTER(Plan)]
     L.moe_grouped_gemm_fp4_plan.restype = i
+    L.moe_grouped_gemm_fp4_workspace_size.argtypes = [i32, i64, i64, i64]
+    L.moe_grouped_gemm_fp4_workspace_size.restype = ctypes.c_size_t
     L.moe_fp4_stage_bytes.argtypes = [i64, i64, i64]
     L.moe_fp4_stage_bytes.restype = i64
     L.moe_fp4_status_string.argtypes = [i]
@@ -90,6 +95,11 @@ def abi_version() -> int:
 
 def stage_bytes(bm: int, bn: int, bk: int) -> int:
     return lib().moe_fp4_stage_bytes(bm, bn, bk)
+
+
+def workspace_size(num_experts: int, m_total: int, n: int, k: int) -> int:
+    """Device workspace bytes of the grouped GEMM for these sizes (always 0)."""
+    return lib().moe_grouped_gemm_fp4_workspace_size(num_experts, m_total, n, k)
 
 
 def plan(num_experts: int, m_total: int, n: int, k: int) -> dict:

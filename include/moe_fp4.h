@@ -1,17 +1,17 @@
 /*
  * moe_fp4.h -- C ABI of the MI355X (gfx950) NVFP4 block-scaled MoE grouped GEMM.
  *
- * The operation: in Mixture-of-Experts decode, each expert's weight matrix is
- * multiplied by the subset of tokens routed to it, so one launch serves many
- * small GEMMs of variable height ("Peering into the CUTLASS Kernel Cache",
- * section "Knowledge Required", the MoE grouped GEMM item; "Peering into the
- * CUTLASS Kernel", section "Input Knowledge Required", item 4).  Operands are
- * NVFP4: 4-bit values packed two per byte with one FP8 scale shared by each
- * block of 16 elements ("Peering into the CUTLASS SharedStorage", section
- * "Input Knowledge", item 3).  Tile M is the tokens of one expert, N the output
- * features, K the reduction dimension (same page, item 5).  Accumulation is
- * FP32 and the output BF16 (same page, "Why This Message Was Written", the
- * epilogue staging estimate).
+ * The operation: in Mixture-of-Experts decode the router sends every token to
+ * a few experts, and each expert multiplies only its own tokens by its weights,
+ * so one launch serves many small GEMMs whose heights differ ("Peering into the
+ * CUTLASS Kernel Cache", section "Knowledge Required", the MoE grouped GEMM
+ * item; "Peering into the CUTLASS Kernel", section "Input Knowledge Required",
+ * item 4).  Operands are NVFP4: 4-bit codes, two to a byte, and an 8-bit float
+ * scale for every 16 consecutive codes ("Peering into the CUTLASS
+ * SharedStorage", section "Input Knowledge", item 3).  Tile M is the tokens of
+ * one expert, N the output features, K the reduction dimension (same page,
+ * item 5).  Accumulation is FP32 and the output BF16 (same page, "Why This
+ * Message Was Written", the epilogue staging estimate).
  *
  * Formats and conventions used by every entry point:
  *   - FP4 element: E2M1 (OCP Microscaling v1.0): magnitudes 0, .5, 1, 1.5, 2,
@@ -101,6 +101,9 @@ enum {
  * 2^-138); below that g underflows to 0 and the block scales are undefined.
  * x, q, sf and tensor_scale must not overlap (q also carries values between
  * the two passes of the DYNAMIC mode).
+ * Block indices are 32-bit integers up to about 2.1e9 blocks and 64-bit above;
+ * the environment variable MOE_FP4_INDEX64=1 selects the 64-bit build for every
+ * size (the same bits; it exists so that build can be tested on small inputs).
  * Errors: NULL (x, q, sf or tensor_scale NULL with rows > 0; tensor_scale
  * NULL always), SHAPE (rows < 0, k <= 0, k % 16, ld_x < k, or x's extent
  * not representable in 64 bits), ALIGN, ARG
@@ -147,8 +150,16 @@ int moe_fp4_quantize(const void* x, int in_dtype, int64_t rows, int64_t k, int64
  *   out          device, [m_total][ldo] BF16 (uint16 bit patterns), 16-byte
  *                aligned; ldo >= n and a multiple of 8.
  *   stream       hipStream_t or NULL.
- * No host synchronisation and no device allocation.  Deterministic: the same
- * inputs give the same output bits (no atomics in the accumulation).
+ * No host synchronisation, no device allocation and no workspace (see
+ * moe_grouped_gemm_fp4_workspace_size).  Deterministic: the same inputs give
+ * the same output bits (no atomics in the accumulation).
+ * Tile choice: by the average rows per expert (moe_grouped_gemm_fp4_plan).  A
+ * workgroup tile whose 128 or 256 output rows span 2^31 - 4096 bytes or more
+ * at this ldo (ldo above about 2^22) is replaced by per-wavefront items of 64
+ * rows, which address one item's rows with 32-bit offsets; the result is the
+ * same to the parity bar.  With the environment variable MOE_FP4_LOG set (not
+ * "0"), each GEMM entry point prints its sizes and chosen tile to stderr
+ * whenever they differ from the previous call's.
  * Errors: NULL, SHAPE (num_experts < 1, m_total < 0, n < 1, k < 1, ldo < n,
  * a_rows < m_total without an index, a_rows < 1 with m_total > 0),
  * ALIGN, UNSUPPORTED (n % 16, k % 256, num_experts > 8192, sizes whose byte
@@ -341,6 +352,21 @@ int moe_fp4_combine(const uint16_t* rows, int64_t ld_rows, int64_t m_total,
                     const int32_t* token_rows, const float* token_weights, int32_t topk,
                     int64_t num_tokens, int64_t n, const float* residual, int64_t ld_res,
                     void* out, int out_dtype, int64_t ldo, void* stream);
+
+/*
+ * moe_grouped_gemm_fp4_workspace_size -- device workspace bytes the grouped GEMM
+ * entry points need for these sizes.  Always 0: every kernel builds its work
+ * list of (expert, M-tile, N-tile) items in LDS from the device offsets, at the
+ * start of each workgroup, so no entry point takes a workspace argument and the
+ * library never allocates.  Kept so that a caller written against a
+ * workspace-taking grouped GEMM can size its buffer the usual way; what passes
+ * validation launches without one ("Peering into the CUTLASS SharedStorage",
+ * section "Why This Message Was Written": a configuration the size check
+ * accepted failed later at initialisation; here there is nothing to fail).
+ * Host only; no GPU call; the arguments are not validated.
+ */
+size_t moe_grouped_gemm_fp4_workspace_size(int32_t num_experts, int64_t m_total, int64_t n,
+                                           int64_t k);
 
 /* Kernel configuration the GEMM picks for a problem (host-only, no GPU call). */
 typedef struct {

@@ -50,6 +50,52 @@ def test_stage_bytes_matches_the_per_stage_transaction_formula():
     assert m.stage_bytes(0, 16, 16) == -1 and m.stage_bytes(16, 16, 8) == -1
 
 
+def test_workspace_size_is_zero():
+    """The work list lives in LDS: no entry point needs a workspace, for any sizes."""
+    m = _lib()
+    for args in [(256, 4096, 512, 6144), (1, 8192, 8192, 8192), (8192, 0, 16, 256), (0, -1, 0, 0)]:
+        assert m.workspace_size(*args) == 0
+
+
+def _log_of_empty_call(monkeypatch, capfd, tile, ldo, E=1, n=1024, k=8192):
+    """Tile line MOE_FP4_LOG prints for a GEMM call with m_total = 0 (validated,
+    logged, nothing launched: fake aligned pointers never reach the GPU)."""
+    m = _lib()
+    monkeypatch.setenv("MOE_FP4_LOG", "1")
+    if tile:
+        monkeypatch.setenv("MOE_FP4_TILE", tile)
+    else:
+        monkeypatch.delenv("MOE_FP4_TILE", raising=False)
+    fake = ctypes.c_void_p(1 << 20)
+    st = m.gemm_raw(fake, fake, fake, 1, None, fake, fake, fake, fake, E, 0, n, k, fake, ldo, None)
+    assert st == 0
+    return capfd.readouterr().err
+
+
+def test_log_prints_the_chosen_tile_and_the_output_range_fallback(monkeypatch, capfd):
+    """MOE_FP4_LOG names the tile; a 256-row workgroup tile whose output rows would
+    span 2^31 - 4096 bytes or more gives way to 64-row per-wave items."""
+    err = _log_of_empty_call(monkeypatch, capfd, "256x256!", 4096)
+    assert "256x256 workgroup tile for every expert" in err, err
+    # 256 rows of ldo BF16 values: 2^31 - 4096 - 4096 bytes, and exactly 2^31 - 4096.
+    err = _log_of_empty_call(monkeypatch, capfd, "256x256!", (2 ** 31 - 4096) // 512 - 8)
+    assert "256x256 workgroup tile for every expert" in err, err
+    err = _log_of_empty_call(monkeypatch, capfd, "256x256!", (2 ** 31 - 4096) // 512)
+    assert "per-wave items" in err and "tile 64x64" in err, err
+    err = _log_of_empty_call(monkeypatch, capfd, "128x128", 2 ** 23 - 24)
+    assert "128x128 workgroup tile" in err, err
+    err = _log_of_empty_call(monkeypatch, capfd, "128x128", 2 ** 23 - 16)
+    assert "per-wave items" in err and "tile 64x64" in err, err
+    err = _log_of_empty_call(monkeypatch, capfd, "128x128", 2 ** 23)
+    assert "per-wave items" in err and "tile 64x64" in err, err
+    # Unset or "0": silent.
+    monkeypatch.setenv("MOE_FP4_LOG", "0")
+    fake = ctypes.c_void_p(1 << 20)
+    assert _lib().gemm_raw(fake, fake, fake, 1, None, fake, fake, fake, fake, 2, 0, 64, 256, fake,
+                           64, None) == 0
+    assert capfd.readouterr().err == ""
+
+
 def test_plan_picks_tiles_by_rows_per_expert(monkeypatch):
     m = _lib()
     monkeypatch.delenv("MOE_FP4_TILE", raising=False)

@@ -101,6 +101,55 @@ def test_largest_ldo():
     _check(bf16_bits_of(out[:, :n]), R, ref, "ldo 2^23")
 
 
+@pytest.mark.parametrize("tile,ldo", [
+    (None, 2 ** 23), ("256x256!", 2 ** 23), ("128x128", 2 ** 23),
+    ("256x256!", (2 ** 31 - 4096) // 512 - 8), ("128x128", 2 ** 23 - 24),
+    (None, (2 ** 31 - 4096) // 512 - 8)])
+def test_workgroup_tiles_at_the_largest_ldo(tile, ldo):
+    """A 300-row expert (two 256-row M-tiles), an empty one and a 17-row one, n = 272
+    (a partial last 256-column N-tile), with output rows ldo apart: at ldo = 2^23 the
+    workgroup tiles' 128 or 256 rows would span 2^31 bytes or more, so the library
+    falls back to per-wave items; just below that bound the workgroup tile itself
+    runs.  Every row is checked, the padding columns and the rows past m_total keep
+    their canary."""
+    E, n, k = 3, 272, 256
+    off = np.array([0, 300, 300, 317], np.int32)
+    m = int(off[-1])
+    extra = 8
+    a_q = gen.random_fp4_bytes((m, k // 2), 61)
+    a_sf = gen.random_e4m3_codes((m, k // 16), 62, 0x20, 0x50)
+    w_q = gen.random_fp4_bytes((E, n, k // 2), 63)
+    w_sf = gen.random_e4m3_codes((E, n, k // 16), 64, 0x20, 0x50)
+    w_scale = np.array([0.5, 1.0, 2.0], np.float32)
+    a_scale = np.float32(1.5)
+    say(f"limits: workgroup tiles, tile={tile}, ldo={ldo}, {(m + extra) * ldo * 2 / 2**30:.1f} GiB output")
+    import os
+    from block_scaled_fp4_05_amd import moe_fp4
+    out = torch.full((m + extra, ldo), -777.0, dtype=torch.bfloat16, device="cuda")
+    old = os.environ.get("MOE_FP4_TILE")
+    if tile:
+        os.environ["MOE_FP4_TILE"] = tile
+    try:
+        moe_fp4.grouped_gemm(dev(a_q), dev(a_sf), dev(np.array([a_scale])), dev(w_q), dev(w_sf),
+                             dev(w_scale), dev(off), out=out, m_total=m)
+        torch.cuda.synchronize()
+    finally:
+        if tile:
+            if old is None:
+                del os.environ["MOE_FP4_TILE"]
+            else:
+                os.environ["MOE_FP4_TILE"] = old
+    canary = int(bf16_bits_of(torch.tensor([-777.0], dtype=torch.bfloat16))[0])
+    cbits = torch.tensor(canary, dtype=torch.int16, device="cuda") if canary < 2 ** 15 else \
+        torch.tensor(canary - 2 ** 16, dtype=torch.int16, device="cuda")
+    assert bool((out[:, n:].view(torch.int16) == cbits).all()), "a padding column was written"
+    assert bool((out[m:, :n].view(torch.int16) == cbits).all()), "a row past m_total was written"
+    R, ref = orc.grouped_gemm(a_q, a_sf, a_scale, w_q, w_sf, w_scale, off)
+    _check(bf16_bits_of(out[:m, :n]), R, ref, f"tile {tile}, ldo {ldo}")
+    del out
+    torch.cuda.empty_cache()
+
+
 def test_byte_offsets_at_the_32_bit_limit():
     """One expert whose weights fill n * k/2 just below 2^31 - 4096 bytes, behind an
     empty expert of the same size (so its base is 2 GB into w_q), and activations of

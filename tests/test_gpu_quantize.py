@@ -206,3 +206,29 @@ def test_dynamic_scale_small_amax_slots(slot):
     b = slot * 96 * 256 + 777
     x[b // nb, (b % nb) * 16] = np.float32(80.0)
     _check(x, torch.bfloat16, label=f"small-matrix amax, largest element in slot {slot}")
+
+
+# The 64-bit block-index build (taken above about 2.1e9 blocks, a 68 GB BF16
+# matrix) run on the shapes that exercise its index arithmetic: the piece and
+# partial-value boundaries, the clamped re-read past the last block and the
+# capped amax slots.  MOE_FP4_INDEX64=1 forces it; the bits must equal the oracle's.
+@pytest.mark.parametrize("rows,k,dtype,slot", [
+    (1, 4080, torch.bfloat16, None), (1, 4112, torch.float32, None), (1025, 8192, torch.bfloat16, None),
+    (4099, 6144, torch.float32, None), (2048, 6144, torch.bfloat16, 5), (512, 6144, torch.bfloat16, 7)])
+def test_index64_build_bit_exact(rows, k, dtype, slot, monkeypatch):
+    monkeypatch.setenv("MOE_FP4_INDEX64", "1")
+    rng = np.random.default_rng(rows * 13 + k)
+    x = rng.standard_normal((rows, k)).astype(np.float32)
+    if dtype == torch.bfloat16:
+        x = gen.bf16_round(x)
+    nb = k // 16
+    if slot is None:
+        x[-1, -1] = np.float32(-57.5)
+    else:
+        # As in the capped and small amax-slot cases above: the largest element in
+        # the block that slot `slot` of one amax thread reads.
+        wgs = 512 if rows * nb >= 256 * 4 * 256 else 96
+        b = slot * wgs * 256 + 777
+        x[b // nb, (b % nb) * 16 + 15] = np.float32(-75.0)
+    _check(x, dtype, label=f"64-bit indices {rows}x{k}")
+    _check(x[:3], dtype, static_g=0.0123, label=f"64-bit indices, static scale, 3x{k}")
