@@ -243,31 +243,44 @@ def measure(prob, steps, warmup):
     for i in range(warmup):
         prob.step(i)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # One event between consecutive steps (and kernels, below): the intervals give
+    # the per-step distribution, the first and last events the mean.
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    e0.record()
+    ev[0].record()
     for i in range(steps):
         prob.step(warmup + i)
-    e1.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    region_ms = e0.elapsed_time(e1)
+    region_ms = ev[0].elapsed_time(ev[-1])
+    step_dist = spread([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
 
     def back_to_back(fn):
         warm(fn)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        evs[0].record()
         for i in range(steps):
             fn(i)
-        b.record()
+            evs[i + 1].record()
         torch.cuda.synchronize()
-        return a.elapsed_time(b) / steps
+        return (evs[0].elapsed_time(evs[-1]) / steps,
+                spread([evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]))
 
-    quant_ms = back_to_back(prob.quantize)
-    gemm_ms = back_to_back(prob.gemm)
+    quant_ms, quant_dist = back_to_back(prob.quantize)
+    gemm_ms, gemm_dist = back_to_back(prob.gemm)
     return dict(wall_ms_per_step=(t1 - t0) * 1e3 / steps, gpu_ms_per_step=region_ms / steps,
-                quant_ms=quant_ms, gemm_ms=gemm_ms)
+                quant_ms=quant_ms, gemm_ms=gemm_ms, step_dist=step_dist, quant_dist=quant_dist,
+                gemm_dist=gemm_dist)
+
+
+def spread(ms):
+    """Median, 10th and 90th percentile of per-launch (or per-step) durations, in us."""
+    import numpy as np
+    a = np.asarray(ms, np.float64) * 1e3
+    return {"median_us": round(float(np.median(a)), 2), "p10_us": round(float(np.percentile(a, 10)), 2),
+            "p90_us": round(float(np.percentile(a, 90)), 2), "n": int(a.size)}
 
 
 def finalize_report(prob, steps):
@@ -596,6 +609,10 @@ def summary(prob, r):
         gbps_step=round((prob.gemm_bytes + prob.quant_bytes) / (ms * 1e-3) / 1e9, 1),
         gemm_us=round(r["gemm_ms"] * 1e3, 2),
         quantize_us=round(r["quant_ms"] * 1e3, 2),
+        # Per launch (per step), from one event between consecutive launches (steps).
+        gemm_us_dist=r["gemm_dist"],
+        quantize_us_dist=r["quant_dist"],
+        step_us_dist=r["step_dist"],
         gemm_tflops=round(prob.flops / gemm_s / 1e12, 2),
         gemm_gbps=round(prob.gemm_bytes / gemm_s / 1e9, 1),
         gemm_hbm_frac=round(prob.gemm_bytes / gemm_s / 1e9 / HBM_PEAK_GBS, 4),
@@ -735,7 +752,8 @@ def main():
     roof = {"bound": "hbm", "kernel": "k_grouped_gemm", "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic, "algorithmic_bytes": int(prob.gemm_bytes),
-            "avg_launch_us": round(r["gemm_ms"] * 1e3, 2)}
+            "avg_launch_us": round(r["gemm_ms"] * 1e3, 2),
+            "median_launch_us": r["gemm_dist"]["median_us"]}
 
     fin = None
     if args.finalize:

@@ -30,9 +30,12 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str | None = None, extra_flags=()) -> str:
     """Always recompiles (each source to an object in parallel, then one link);
-    writes the library atomically."""
+    writes the library atomically to `out` (default: the in-tree library).
+    `extra_flags` go on every compile and the link (the host-sanitizer build of
+    the CPU tests passes -Xarch_host flags here)."""
+    out = out or LIB
     from concurrent.futures import ThreadPoolExecutor
     import tempfile
 
@@ -41,7 +44,7 @@ def build(verbose: bool = False) -> str:
     with tempfile.TemporaryDirectory(prefix="moe_fp4_build_") as tmpdir:
         def compile_one(src):
             obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
-            cmd = [cc, *[f for f in HIPCC_FLAGS if f != "-shared"], *inc, "-c",
+            cmd = [cc, *[f for f in HIPCC_FLAGS if f != "-shared"], *extra_flags, *inc, "-c",
                    os.path.join(CSRC, src), "-o", obj]
             return obj, subprocess.run(cmd, capture_output=True, text=True)
 
@@ -53,15 +56,16 @@ def build(verbose: bool = False) -> str:
             log.append(res.stdout + res.stderr)
             if res.returncode != 0:
                 raise RuntimeError(f"hipcc failed on {src}:\n" + res.stdout + res.stderr)
-        tmp = LIB + ".tmp%d" % os.getpid()
-        link = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", *[o for o, _ in results], "-o", tmp]
+        tmp = out + ".tmp%d" % os.getpid()
+        link = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", *extra_flags,
+                *[o for o, _ in results], "-o", tmp]
         res = subprocess.run(link, capture_output=True, text=True)
         if res.returncode != 0:
             raise RuntimeError("link failed:\n" + res.stdout + res.stderr)
         if verbose:
             print("".join(log) + res.stderr)
-        os.replace(tmp, LIB)
-    return LIB
+        os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -9,13 +9,15 @@
  *   - 4-bit values, two per byte ("Peering into the CUTLASS Kernel Cache",
  *     section "Knowledge Required"; "Peering into the CUTLASS SharedStorage",
  *     section "Input Knowledge", item 3);
- *   - one FP8 scale per 16 elements (same page 4 item; the "Vs16" schedule name
- *     in "Peering into the CUTLASS Kernel", section "Mistakes and Incorrect
- *     Assumptions");
- *   - grouped problem: each expert's weights times the subset of tokens routed
- *     to it, variable group sizes (page 1, "Knowledge Required", MoE item);
- *   - FP32 accumulation, BF16 output staging (page 4, "Why This Message Was
- *     Written", the epilogue estimate).
+ *   - one FP8 scale per 16 elements ("Peering into the CUTLASS SharedStorage",
+ *     section "Input Knowledge", item 3; the "Vs16" schedule name in "Peering
+ *     into the CUTLASS Kernel", section "Mistakes and Incorrect Assumptions");
+ *   - grouped problem: every expert's weights meet only the tokens routed to
+ *     that expert, so the group heights vary ("Peering into the CUTLASS Kernel
+ *     Cache", section "Knowledge Required", the MoE grouped GEMM item);
+ *   - FP32 accumulation, BF16 output staging ("Peering into the CUTLASS
+ *     SharedStorage", section "Why This Message Was Written", the epilogue
+ *     estimate).
  * Element format E2M1 and scale format E4M3 follow the OCP Microscaling (MX)
  * v1.0 and OCP 8-bit Floating Point (OFP8) v1.0 specifications.  The scale
  * recipe (amax / (6*448) tensor scale, RNE block scale, IEEE division) is a
@@ -252,9 +254,10 @@ static int owner_expert(const int32_t* off, int32_t num_experts, int64_t r) {
  * w_sf [E][n][k/16]; element 2i in the low nibble of byte i.
  * The sum is formed exactly: per 16-block, sum_k (2a)(2w) is an integer, times
  * (512 sa)(512 sw), accumulated in int64; the value is acc * 2^-20.  It is then
- * scaled in double.  The grouped problem ("each expert's weight matrix is
- * multiplied by a subset of tokens", page 1 "Knowledge Required"; one launch
- * for many expert GEMMs, page 2 "Input Knowledge Required" item 4).
+ * scaled in double.  The grouped problem: one product per expert over the rows
+ * routed to it ("Peering into the CUTLASS Kernel Cache", section "Knowledge
+ * Required", the MoE grouped GEMM item), all experts in one call ("Peering into
+ * the CUTLASS Kernel", section "Input Knowledge Required", item 4).
  * Only the listed output rows (rows_sel[0..nsel), or all m_total rows when
  * rows_sel is NULL) are computed; R_out and bf16_out are indexed
  * [sel_index][n].  Either output may be NULL.  Returns 0 or -1. */
