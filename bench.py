@@ -243,30 +243,27 @@ def measure(prob, steps, warmup):
     for i in range(warmup):
         prob.step(i)
     torch.cuda.synchronize()
-    # One event between consecutive steps (and kernels, below): the intervals give
-    # the per-step distribution, the first and last events the mean.
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev[0].record()
+    e0.record()
     for i in range(steps):
         prob.step(warmup + i)
-        ev[i + 1].record()
+    e1.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    region_ms = ev[0].elapsed_time(ev[-1])
-    step_dist = spread([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+    region_ms = e0.elapsed_time(e1)
+    step_dist = grouped(prob.step, steps, warmup)
 
     def back_to_back(fn):
         warm(fn)
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-        evs[0].record()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
         for i in range(steps):
             fn(i)
-            evs[i + 1].record()
+        b.record()
         torch.cuda.synchronize()
-        return (evs[0].elapsed_time(evs[-1]) / steps,
-                spread([evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]))
+        return a.elapsed_time(b) / steps, grouped(fn, steps)
 
     quant_ms, quant_dist = back_to_back(prob.quantize)
     gemm_ms, gemm_dist = back_to_back(prob.gemm)
@@ -275,8 +272,29 @@ def measure(prob, steps, warmup):
                 gemm_dist=gemm_dist)
 
 
+def grouped(fn, calls, first=0, groups=10):
+    """Spread of per-call durations: `calls` back-to-back calls in `groups` equal
+    groups with one HIP event between groups (an event between every two calls
+    adds a few microseconds to each on this part), each group giving its mean per
+    call.  A separate pass from the timed one."""
+    import torch
+    per = max(1, calls // groups)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(groups + 1)]
+    ev[0].record()
+    i = first
+    for gi in range(groups):
+        for _ in range(per):
+            fn(i)
+            i += 1
+        ev[gi + 1].record()
+    torch.cuda.synchronize()
+    r = spread([ev[gi].elapsed_time(ev[gi + 1]) / per for gi in range(groups)])
+    r["calls_per_group"] = per
+    return r
+
+
 def spread(ms):
-    """Median, 10th and 90th percentile of per-launch (or per-step) durations, in us."""
+    """Median, 10th and 90th percentile of durations given in ms, in us."""
     import numpy as np
     a = np.asarray(ms, np.float64) * 1e3
     return {"median_us": round(float(np.median(a)), 2), "p10_us": round(float(np.percentile(a, 10)), 2),
@@ -609,7 +627,7 @@ def summary(prob, r):
         gbps_step=round((prob.gemm_bytes + prob.quant_bytes) / (ms * 1e-3) / 1e9, 1),
         gemm_us=round(r["gemm_ms"] * 1e3, 2),
         quantize_us=round(r["quant_ms"] * 1e3, 2),
-        # Per launch (per step), from one event between consecutive launches (steps).
+        # Per launch (per step): median, p10, p90 over 10 groups of back-to-back calls.
         gemm_us_dist=r["gemm_dist"],
         quantize_us_dist=r["quant_dist"],
         step_us_dist=r["step_dist"],

@@ -6,7 +6,9 @@
 
 #include <stdio.h>
 #include <stdlib.h>
+#include <string.h>
 
+#include <cstring>
 #include <map>
 #include <mutex>
 #include <string>
@@ -55,15 +57,25 @@ GemmTile choose_tile(int32_t num_experts, int64_t m_total, int64_t n, int64_t k,
   // kBigRows rows take 256 x 256 items and the rest the per-wave kernel (two
   // launches over disjoint experts, chosen on the device from the offsets);
   // else every expert takes 128 x 128 items.
-  if (avg >= 96) t = big_lds(num_experts) <= kLdsBytes ? GemmTile{16, 16, 8, 1, 0, 2}
-                                                        : GemmTile{8, 8, 4, 1, 0, 1};
+  // A single expert takes the large tile in one launch (the per-wave launch of
+  // the split would find no expert to run and still cost its few microseconds).
+  if (avg >= 96) t = big_lds(num_experts) <= kLdsBytes
+                         ? GemmTile{16, 16, 8, 1, 0, num_experts == 1 ? 3 : 2}
+                         : GemmTile{8, 8, 4, 1, 0, 1};
   if (k % 512 == 0) t.k_sub = 2;
   t.lds_scales = k % kSpan == 0 ? 1 : 0;
   // "256x256!": every expert in 256 x 256 items, however few its rows.
-  if (env && env[0] == '2' && env[1] == '5' && env[2] == '6' && env[3] == 'x' && env[4] == '2' &&
-      env[5] == '5' && env[6] == '6' && env[7] == '!' && env[8] == '\0') {
-    if (big_lds(num_experts) <= kLdsBytes) t = GemmTile{16, 16, 8, 1, 0, 3};
-    return t;
+  // "256x256f8" and "256x256f8!": the same with the split-K FP8 inner product.
+  if (env && std::strncmp(env, "256x256", 7) == 0 && env[7] != '\0') {
+    const char* rest = env + 7;
+    const bool f8 = rest[0] == 'f' && rest[1] == '8';
+    if (f8) rest += 2;
+    const bool all = rest[0] == '!' && rest[1] == '\0';
+    if ((all || (f8 && rest[0] == '\0')) && big_lds(num_experts) <= kLdsBytes) {
+      t = GemmTile{16, 16, 8, 1, 0, all ? 3 : 2};
+      t.f8 = f8 ? 1 : 0;
+    }
+    if (all || f8) return t;
   }
   if (env && *env) {
     // "MxN" or "MxNxK", optionally followed by 'r' (weight scales through
@@ -126,9 +138,12 @@ void log_tile(const char* entry, int32_t num_experts, int64_t m_total, int64_t n
   static std::mutex mu;
   static std::string last;
   char line[320];
-  const char* kind = t.tiled == 3 ? "256x256 workgroup tile for every expert"
-                     : t.tiled == 2 ? "256x256 workgroup tile for experts of >= 96 rows, "
-                                      "16x64 per-wave items for the rest"
+  const char* kind = t.tiled == 3 ? (t.f8 ? "256x256 workgroup tile (FP8 split-K) for every expert"
+                                           : "256x256 workgroup tile for every expert")
+                     : t.tiled == 2 ? (t.f8 ? "256x256 workgroup tile (FP8 split-K) for experts of "
+                                              ">= 96 rows, 16x64 per-wave items for the rest"
+                                            : "256x256 workgroup tile for experts of >= 96 rows, "
+                                              "16x64 per-wave items for the rest")
                      : t.tiled == 1 ? "128x128 workgroup tile" : "per-wave items";
   snprintf(line, sizeof line,
            "moe_fp4: %s E=%d m_total=%lld n=%lld k=%lld ldo=%lld: %s (tile %dx%d, k step %d, "
@@ -201,13 +216,13 @@ GemmTile small_expert_tile(int64_t k) {
 }
 
 hipError_t launch_grouped_gemm(const GemmArgs& p, const GemmTile& t, hipStream_t stream) {
-  if (t.tiled == 3) return launch_grouped_gemm_big(p, stream);
+  if (t.tiled == 3) return launch_grouped_gemm_big(p, t.f8 != 0, stream);
   if (t.tiled == 2) {
     // Experts with kBigRows rows or more in 256 x 256 items, the rest per wave.
     GemmArgs big = p, small = p;
     big.rows_lo = kBigRows;
     big.n_tiles = (int32_t)((p.n + 255) / 256);
-    hipError_t err = launch_grouped_gemm_big(big, stream);
+    hipError_t err = launch_grouped_gemm_big(big, t.f8 != 0, stream);
     if (err != hipSuccess) return err;
     const GemmTile s = small_expert_tile(p.k);
     small.rows_hi = kBigRows;

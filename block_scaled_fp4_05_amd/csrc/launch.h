@@ -26,6 +26,8 @@ struct GemmTile {
                    // items (grouped_gemm_tiled.hip); 2 = 256 x 256 items
                    // (grouped_gemm_big.hip) for experts of kBigRows rows or more
                    // and the per-wave kernel for the rest; 3 = 256 x 256 for all
+  int f8 = 0;      // 256 x 256 items: split K by scale block on the FP8 MFMA
+                   // instead of dequantising to FP16 (MOE_FP4_TILE "256x256f8")
 };
 
 constexpr int kKStep = 256;  // K granularity the kernels require
@@ -134,8 +136,9 @@ hipError_t launch_grouped_gemm_swiglu(const GemmArgs& args, const GemmTile& tile
 hipError_t launch_grouped_gemm_tiled(const GemmArgs& args, hipStream_t stream);
 size_t tiled_lds(int32_t num_experts);
 
-// Large-tile kernel (grouped_gemm_big.hip): 256 x 256 items, 4 waves of 128 x 128.
-hipError_t launch_grouped_gemm_big(const GemmArgs& args, hipStream_t stream);
+// Large-tile kernel (grouped_gemm_big.hip): 256 x 256 items, 8 waves of 128 x 64;
+// f8: the split-K-by-scale-block FP8 variant.
+hipError_t launch_grouped_gemm_big(const GemmArgs& args, bool f8, hipStream_t stream);
 size_t big_lds(int32_t num_experts);
 
 // LDS a workgroup may use on gfx950.

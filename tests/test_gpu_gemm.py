@@ -84,7 +84,8 @@ def _check_rows(got_bits, P, rows_sel=None, a_row_index=None, label=""):
     return float(err.max()) if err.size else 0.0
 
 
-TILES = ["16x64", "32x64", "64x64", "16x32", "32x32", "64x32", "128x128", "256x256", "256x256!"]
+TILES = ["16x64", "32x64", "64x64", "16x32", "32x32", "64x32", "128x128", "256x256", "256x256!",
+         "256x256f8", "256x256f8!"]
 
 
 @pytest.mark.parametrize("tile", TILES)
@@ -193,6 +194,38 @@ def test_full_size_workload_sampled_rows(name, count):
     assert not np.any(got == bf16_bits_of(torch.tensor([-777.0], dtype=torch.bfloat16))[0])
 
 
+@pytest.mark.parametrize("name,tile", [("c2", None), ("c2", "256x256f8"), ("c5", None),
+                                       ("c5", "256x256f8")])
+def test_large_tile_rows_of_every_m_tile(name, tile):
+    """The 256 x 256 tile at full size, rows of every 256-row M-tile of every expert
+    that takes it, cycling through the 8 32-row MFMA block positions of the tile's
+    two 128-row wave halves, plus each such expert's first and last row: c2, all 8
+    block positions of each of the 32 M-tiles of the dense product (258 rows of 8192
+    columns); c5, two rows of each M-tile of the 59 experts of 96 rows or more.  On
+    the FP16 dequantised path (default) and on the split-K FP8 path."""
+    P, idx = _workload_problem(name)
+    sel = wl_data.large_tile_rows(P["offsets"], 41, per_tile=8 if name == "c2" else 2)
+    say(f"gemm workload {name} tile={tile}: {len(sel)} rows of the large tile")
+    got = _gpu_gemm(P, a_row_index=idx, tile=tile)
+    _check_rows(got, P, rows_sel=sel, a_row_index=idx, label=f"{name} {tile}")
+
+
+def test_fp8_split_k_tile_agrees_with_the_fp16_tile():
+    """Both large-tile paths add each 16-element block's exact sum into an FP32
+    accumulator; they may round differently only where the MFMA's internal
+    accumulation does.  Every row of a mid-size problem meets the bar on both, and
+    the two outputs agree to within one BF16 unit in the last place."""
+    P = _random_problem(2, [384, 200], 512, 2048, 4242)
+    say("gemm 256x256 vs 256x256f8, E=2 rows=[384, 200] n=512 k=2048")
+    a = _gpu_gemm(P, tile="256x256!")
+    b = _gpu_gemm(P, tile="256x256f8!")
+    _check_rows(a, P, label="256x256!")
+    _check_rows(b, P, label="256x256f8!")
+    fa, fb = orc.bf16_bits_to_float(a), orc.bf16_bits_to_float(b)
+    ulp = np.abs(fa) * 2.0 ** -7 + 1e-30
+    assert np.all(np.abs(fa - fb) <= ulp), "the two paths differ by more than one BF16 ulp"
+
+
 def test_quantise_then_gemm_chain_c3():
     """Quantise the c3 tokens on the GPU and feed the GEMM; compare with the oracle
     chain started from the same raw activations."""
@@ -249,7 +282,7 @@ WG_CASES = [(2, [300, 520], 320, 1024), (3, [257, 0, 40], 272, 512), (1, [600], 
             (5, [95, 96, 97, 0, 1], 192, 512)]
 
 
-@pytest.mark.parametrize("tile", ["128x128", "256x256", "256x256!"])
+@pytest.mark.parametrize("tile", ["128x128", "256x256", "256x256!", "256x256f8", "256x256f8!"])
 @pytest.mark.parametrize("case", range(len(WG_CASES)))
 def test_workgroup_tiles_several_tiles_per_expert(case, tile):
     E, rows, n, k = WG_CASES[case]

@@ -44,3 +44,27 @@ def sample_rows(offsets: np.ndarray, count: int, seed: int) -> np.ndarray:
     while len(picks) < count:
         picks.add(int(rng.integers(0, m)))
     return np.array(sorted(picks), dtype=np.int64)
+
+
+def large_tile_rows(offsets: np.ndarray, seed: int, per_tile: int = 2, min_rows: int = 96) -> np.ndarray:
+    """Rows that cover the 256 x 256 workgroup tile of every expert with at least
+    `min_rows` rows: `per_tile` rows in each 256-row M-tile, cycling through the 8
+    32-row MFMA block positions of the tile's two 128-row wave halves (position
+    i = row % 256 // 32), at a random row within the block, plus each such
+    expert's first and last row."""
+    rng = np.random.default_rng(seed)
+    picks = set()
+    pos = 0
+    for e in range(len(offsets) - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi - lo < min_rows:
+            continue
+        picks.update((lo, hi - 1))
+        for t0 in range(lo, hi, 256):
+            for _ in range(per_tile):
+                block = pos % 8
+                pos += 1
+                r = t0 + 32 * block + int(rng.integers(0, 32))
+                if r < hi:
+                    picks.add(r)
+    return np.array(sorted(picks), dtype=np.int64)
