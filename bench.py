@@ -365,9 +365,24 @@ def finalize_report(prob, steps):
     def lib_combine(i):
         moe_fp4.combine(prob.out, token_rows, token_weights, out=combined)
 
+    # The device's FP32 atomic-add rate on the most favourable pattern: every
+    # wavefront adds into 256 contiguous bytes (torch's index_add_ over a flat
+    # buffer, each element hit twice), as many adds as the fused epilogue makes.
+    n_adds = prob.m_total * w.n
+    flat = torch.zeros((n_adds + 1) // 2, dtype=torch.float32, device=dev)
+    flat_idx = torch.arange(n_adds, device=dev, dtype=torch.int64) % flat.numel()
+    flat_src = torch.ones(n_adds, dtype=torch.float32, device=dev)
+
+    def atomics(i):
+        flat.index_add_(0, flat_idx, flat_src)
+
     res = dict(fused_us=round(timed(fused), 2), zero_us=round(timed(zero), 2),
                plain_gemm_us=round(timed(plain), 2), combine_us=round(timed(lib_combine), 2),
                torch_index_add_us=round(timed(combine), 2))
+    res["atomic_adds"] = n_adds
+    res["coalesced_atomic_adds_us"] = round(timed(atomics), 2)
+    res["coalesced_atomic_gadds_per_s"] = round(n_adds / (res["coalesced_atomic_adds_us"] * 1e-6) / 1e9, 1)
+    del flat, flat_idx, flat_src
     comb_bytes = prob.m_total * w.n * 2 + w.tokens * w.n * 2 + w.tokens * topk * 8
     res["combine_gbps"] = round(comb_bytes / (res["combine_us"] * 1e-6) / 1e9, 1)
     # Parity of one fused call against the unfused pipeline on the same inputs (the

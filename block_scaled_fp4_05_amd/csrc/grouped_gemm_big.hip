@@ -72,6 +72,39 @@ __device__ __forceinline__ void dequant_chunk(uint8_t* stage, int row, const Row
   put_chunk(stage, row, w, dequant8(w < 4 ? r.q0[w & 3] : r.q1[w & 3], sc));
 }
 
+// Items of one expert in banded order: its M-tiles are taken in bands of
+// kBand, and a band's items run N-tile by N-tile, M-tile fastest.  Workgroups
+// with consecutive logical numbers share an XCD and its L2 (logical_block), so
+// the 32 items an XCD runs side by side form a kBand x 8 block of the output:
+// 4 activation strips and 8 weight strips read through one L2, where an N-tile
+// per XCD (the plain N-major order) reads 32 activation strips and 1 weight
+// strip.  On the dense 8192^3 case that cuts the strips fetched per round from
+// 33 to 12 per XCD.  A bijection on the expert's items; experts of kBand
+// M-tiles or fewer keep the plain order.
+constexpr int kBand = 4;
+
+__device__ __forceinline__ ItemPos locate_banded(int32_t i, int32_t from, const WorkList& wl,
+                                                 const GemmArgs& p, int lane) {
+  const int32_t e = find_expert(i, from, wl, p.num_experts, lane);
+  const int32_t r_lo = uniform(wl.off[e]);
+  const int32_t cnt = uniform(wl.off[e + 1]) - r_lo;
+  const int32_t mts = (cnt + kBM - 1) / kBM;
+  const int32_t local = i - uniform(wl.prefix[e]);
+  const int32_t band_items = kBand * p.n_tiles;
+  const int32_t band = local / band_items, within = local - band * band_items;
+  const int32_t left = mts - band * kBand;
+  const int32_t tall = left < kBand ? left : kBand;  // M-tiles in this band
+  const int32_t nt = within / tall, mt = band * kBand + (within - nt * tall);
+  ItemPos it;
+  it.e = e;
+  it.row0 = r_lo + mt * kBM;
+  const int32_t rows_left = cnt - mt * kBM;
+  it.rows_valid = rows_left < kBM ? rows_left : kBM;
+  it.n0 = nt * kBN;
+  it.alpha = ((sconst_f32)p.a_scale)[0] * ((sconst_f32)p.w_scale)[e];
+  return it;
+}
+
 // One operand row of an item for one loader thread: its buffer resources and
 // byte offsets, and where stage st's codes start.
 struct OperandRow {
@@ -233,7 +266,7 @@ void k_grouped_gemm_big(const GemmArgs p) {
   int32_t from = 0;
   for (int32_t j = 0; j < my_items; ++j) {
     const int32_t item = j * nblk + (j == rounds - 1 ? lb_last : lb_full);
-    const ItemPos it = locate(item, from, wl, p, kBM, kBN, lane);
+    const ItemPos it = locate_banded(item, from, wl, p, lane);
     from = it.e;
 
     const OperandRow orow = operand_row(p, it, is_w, wave, lrow);
@@ -432,7 +465,7 @@ void k_grouped_gemm_big_f8(const GemmArgs p) {
   int32_t from = 0;
   for (int32_t j = 0; j < my_items; ++j) {
     const int32_t item = j * nblk + (j == rounds - 1 ? lb_last : lb_full);
-    const ItemPos it = locate(item, from, wl, p, kBM, kBN, lane);
+    const ItemPos it = locate_banded(item, from, wl, p, lane);
     from = it.e;
     const OperandRow orow = operand_row(p, it, is_w, wave, lrow);
 
