@@ -172,7 +172,33 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const void* x, int64_t ro
     const uint32_t sfb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(r, r, 0, false) & 0xFFu;
     const float s = __builtin_amdgcn_cvt_f32_fp8(sfb, 0) * g;
     uint32_t packed[2] = {0u, 0u};
-    if (s != 0.0f) {
+    if (s >= 0x1p-100f && s <= 0x1p125f) {
+      // The 16 quotients x / s share their divisor: one IEEE division gives
+      // rs = RN(1/s), and each quotient is q = RN(x * rs) corrected once with
+      // the exact residual, y = RN(q + RN(x - q s) * rs), Markstein's
+      // correction, which equals RN(x / s) when rs = RN(1/s) and the residual
+      // is exact.  With s >= 2^-100 the residual is exact for every quotient
+      // of magnitude 2^-3 or more, the only ones whose E2M1 code is not zero;
+      // smaller ones stay smaller and keep x's sign (s > 0, so the quotient's
+      // sign is x's), which is all their code depends on.  q is clamped to
+      // [-8, 8] first: from 8 up the code saturates anyway, and a quotient
+      // that overflows (a static scale far below the data) then stays finite.
+      // Checked on the CPU against the IEEE quotient's code on 2.1e9 pairs.
+      const float rs = 1.0f / s;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float y[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float x = v[2 * i + h];
+          const float q = __builtin_fminf(__builtin_fmaxf(x * rs, -8.0f), 8.0f);
+          y[h] = __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q, s, x), rs, q), x);
+        }
+        // The hardware E2M1 conversion: nearest even, saturating, sign kept.
+        const uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y[0], y[1], 1.0f, 0) & 0xFFu;
+        packed[i >> 2] |= c << (8 * (i & 3));
+      }
+    } else if (s != 0.0f) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         // IEEE division (the compiler's correctly rounded sequence), then the
