@@ -26,6 +26,7 @@ the same thing).
   python bench.py --finalize   # + finalize: fused atomics vs plain GEMM + token-order combine
   python bench.py --layer      # + a whole MoE FFN layer (eager and from a HIP graph)
   python bench.py --copy-calibration   # a plain copy of known size, for counter scaling
+  python bench.py --ceilings           # torch's read / write / copy rates on 1 GiB
 """
 from __future__ import annotations
 
@@ -76,6 +77,8 @@ def parse_args():
                     help="also time a whole MoE FFN layer on this shard: quantise, gate+up GEMM "
                          "with the SwiGLU + NVFP4 epilogue, down-projection GEMM, token-order "
                          "combine (the workload's weights are the gate+up projection)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only print torch's read, write and copy rates on 1 GiB (streaming context)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a device copy of known size (counter scale factor)")
     return ap.parse_args()
@@ -740,6 +743,34 @@ def parity(got, R, ref):
 
 # -------------------------------------------------------------------- main --
 
+def ceilings():
+    """Streaming rates of this GPU with torch's own kernels, as context for the roofline
+    fractions: a read of 1 GiB (a sum), a write of 1 GiB (a fill) and a copy of 1 GiB
+    (1 GiB read + 1 GiB written), each the mean of back-to-back calls after a 0.25 s warm-up."""
+    import torch
+    nbytes = 1 << 30
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    out = {}
+
+    def rate(fn, traffic):
+        warm(lambda i: fn())
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / 20 * 1e3
+        return {"us": round(us, 1), "gbps": round(traffic / (us * 1e-6) / 1e9, 1)}
+
+    out["read_1GiB_sum"] = rate(lambda: a.sum(), nbytes)
+    out["write_1GiB_fill"] = rate(lambda: b.fill_(2.0), nbytes)
+    out["copy_1GiB"] = rate(lambda: b.copy_(a), 2 * nbytes)
+    out["peak_gbps"] = HBM_PEAK_GBS
+    print(json.dumps({"ceilings": out}), flush=True)
+
+
 def copy_calibration():
     import torch
     nbytes = 1 << 30
@@ -767,6 +798,9 @@ def main():
     moe_fp4.lib()  # the HIP library must be built: there is no fallback
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.ceilings:
+        ceilings()
         return
 
     want_cpu = not args.no_cpu_baseline
