@@ -14,17 +14,22 @@
 // of amax, the maximum of the per-workgroup values fl(amax_wg / 2688) is g
 // itself (0 for an all-zero matrix, for which g = 1).  The quantise launch is
 // laid out so that its workgroup w writes, in its first pass, the codes of
-// blocks [256 w, 256 w + 256): 2 KB of q that no other workgroup touches.  The
-// amax launch writes its P partial values into the first P floats of every
-// such 2 KB piece (P <= 512 workgroups, at most 2048 pieces); each quantise
+// blocks [256 w, 256 w + 256): 2 KB of q that no other workgroup touches (the
+// other blocks of that pass lie past the first `pieces` pieces).  The amax
+// launch writes its P partial values into the first P floats of every such
+// 2 KB piece (P <= 256 workgroups, at most 512 pieces); each quantise
 // workgroup reduces the copy in its own piece, and only after a barrier that
 // follows the reduction does it overwrite the piece with codes.  Workgroup 0
 // also publishes g to the caller's tensor_scale.  A matrix of fewer than 256
-// blocks takes one workgroup in each launch and one partial value.
+// blocks takes one workgroup in each launch and one partial value.  The copies
+// are scattered 4-byte stores, P per piece: with 512 partial values and 2048
+// pieces they took 7 us of the amax launch on 4096 x 6144 BF16 values, hence
+// the lower caps.
 //
-// One thread quantises one 16-element block: 32 (BF16) or 64 (FP32) bytes in,
-// 8 bytes of codes and 1 scale byte out, consecutive threads on consecutive
-// blocks of a row, so every access is coalesced.  The pass is HBM-bound:
+// One thread quantises one 16-element block at a time: 32 (BF16) or 64 (FP32)
+// bytes in, 8 bytes of codes and 1 scale byte out, consecutive threads on
+// consecutive blocks of a row, so every access is coalesced; each pass loads
+// kQuantBlocks blocks per thread before encoding them.  The pass is HBM-bound:
 // (2 or 4) + 0.5625 bytes per element.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -70,24 +75,25 @@ __global__ void k_set_one(float* ts) {
 }
 
 // Blocks per thread per iteration of the amax pass: all their loads are in
-// flight before the reduction.  A matrix that would give fewer workgroups than
-// CUs at kAmaxBlocks takes kAmaxBlocksSmall, in half as many workgroups.
-// Measured on the 512 x 6144 BF16 decode activations (one pass per thread):
-// 96 workgroups of 8 blocks per thread run the two launches in 8.4 us, against
-// 8.8 us for 192 of 4, 9.7 for 384 of 2 and 9.7 for 48 of 16.
-constexpr int kAmaxBlocks = 4;
-constexpr int kAmaxBlocksSmall = 8;
+// flight before the reduction.  Measured on the 512 x 6144 BF16 decode
+// activations (one pass per thread): 96 workgroups of 8 blocks per thread run
+// the two launches in 8.4 us, against 8.8 us for 192 of 4, 9.7 for 384 of 2
+// and 9.7 for 48 of 16.
+constexpr int kAmaxBlocks = 8;
+// Blocks per thread per iteration of the quantise pass.
+constexpr int kQuantBlocks = 4;
 // Blocks of one quantise workgroup's first pass, and the floats of q they
 // cover (8 bytes of codes per block): room for this many partial values.
 constexpr int kPiece = kThreads;
 constexpr int kPieceFloats = kPiece * 8 / 4;
 // Launch limits of the dynamic path: at most kMaxPartials amax workgroups and
 // kMaxPieces quantise workgroups, so the amax launch writes at most
-// kMaxPartials * kMaxPieces floats of partial values.
-constexpr int kMaxPartials = kPieceFloats;
-constexpr int kMaxPieces = 2048;
-// Compute units of the MI355X.
-constexpr int kCus = 256;
+// kMaxPartials * kMaxPieces floats of partial values.  Measured on 4096 x 6144
+// and 8192 x 8192 BF16 values (amax + quantise): 256 and 512, 24.2 and 51.9 us;
+// 512 and 2048 with 4 amax blocks and 1 quantise block per thread, 29.4 and
+// 57.3 us; 512 and 512, 24.9 and 53.0; 512 and 256, 26.0 and 57.4.
+constexpr int kMaxPartials = kPieceFloats / 2;
+constexpr int kMaxPieces = 512;
 
 // Block-wide maximum of one float per thread (all threads must call it).
 __device__ __forceinline__ float block_max(float m, float* wave_max) {
@@ -159,10 +165,25 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const void* x, int64_t ro
   const float six_g = 6.0f * g;
   const I nb = (I)(k / 16);
   const I total = (I)rows * nb;
-  for (I blk = (I)blockIdx.x * kThreads + threadIdx.x; blk < total; blk += (I)gridDim.x * kThreads) {
-    const I row = blk / nb, b = blk - row * nb;
-    float v[16];
-    load_block16<DT, I>(x, row, ld_x, b, v);
+  const I stride = (I)gridDim.x * kThreads;
+  for (I blk0 = (I)blockIdx.x * kThreads + threadIdx.x; blk0 < total;
+       blk0 += (I)kQuantBlocks * stride) {
+    // All kQuantBlocks loads first (past the end, the last block again, unused).
+    float vb[kQuantBlocks][16];
+    I rowj[kQuantBlocks], bj[kQuantBlocks];
+#pragma unroll
+    for (int j = 0; j < kQuantBlocks; ++j) {
+      I blk = blk0 + (I)j * stride;
+      blk = blk < total ? blk : total - 1;
+      rowj[j] = blk / nb;
+      bj[j] = blk - rowj[j] * nb;
+      load_block16<DT, I>(x, rowj[j], ld_x, bj[j], vb[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < kQuantBlocks; ++j) {
+    if (blk0 + (I)j * stride >= total) break;
+    const I row = rowj[j], b = bj[j];
+    const float (&v)[16] = vb[j];
     float amax_b = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) amax_b = fmaxf(amax_b, fabsf(v[i]));
@@ -211,6 +232,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const void* x, int64_t ro
     *reinterpret_cast<u32x2_t*>(q + (int64_t)row * (k / 2) + (int64_t)b * 8) =
         u32x2_t{packed[0], packed[1]};
     sf[(int64_t)row * nb + b] = (uint8_t)sfb;
+    }
   }
 }
 
@@ -225,28 +247,22 @@ hipError_t launch_dt(const void* x, int64_t rows, int64_t k, int64_t ld_x, uint8
       // Quantise workgroups: one whole 256-block piece each in the first pass
       // (the rest of the blocks follow in grid-stride passes), at most
       // kMaxPieces.  Amax workgroups: each thread covers kAmaxBlocks blocks
-      // per pass (kAmaxBlocksSmall below one workgroup per CU at that rate),
-      // at most kMaxPartials; a matrix below one piece takes one.
+      // per pass, at most kMaxPartials; a matrix below one piece takes one.
       int64_t pieces = total / kPiece;
       if (pieces > kMaxPieces) pieces = kMaxPieces;
       int64_t parts = (want + kAmaxBlocks - 1) / kAmaxBlocks;
-      const bool small = parts < kCus;
-      if (small) parts = (want + kAmaxBlocksSmall - 1) / kAmaxBlocksSmall;
       if (parts > kMaxPartials) parts = kMaxPartials;
       if (pieces < 1) pieces = parts = 1;
-      if (small)
-        hipLaunchKernelGGL((k_amax<DT, I, kAmaxBlocksSmall>), dim3((unsigned)parts), dim3(kThreads),
-                           0, stream, x, rows, k, ld_x, reinterpret_cast<float*>(q), (int)pieces);
-      else
-        hipLaunchKernelGGL((k_amax<DT, I, kAmaxBlocks>), dim3((unsigned)parts), dim3(kThreads), 0,
-                           stream, x, rows, k, ld_x, reinterpret_cast<float*>(q), (int)pieces);
+      hipLaunchKernelGGL((k_amax<DT, I, kAmaxBlocks>), dim3((unsigned)parts), dim3(kThreads), 0,
+                         stream, x, rows, k, ld_x, reinterpret_cast<float*>(q), (int)pieces);
       hipLaunchKernelGGL((k_quantize<DT, true, I>), dim3((unsigned)pieces), dim3(kThreads), 0,
                          stream, x, rows, k, ld_x, q, sf, ts, (int)parts);
     } else {
       hipLaunchKernelGGL(k_set_one, dim3(1), dim3(64), 0, stream, ts);
     }
   } else if (total > 0) {
-    const int grid = (int)(want < 65536 ? want : 65536);
+    const int64_t groups = (want + kQuantBlocks - 1) / kQuantBlocks;
+    const int grid = (int)(groups < 65536 ? groups : 65536);
     hipLaunchKernelGGL((k_quantize<DT, false, I>), dim3(grid), dim3(kThreads), 0, stream, x, rows,
                        k, ld_x, q, sf, ts, 0);
   }
@@ -261,7 +277,8 @@ template <int DT>
 hipError_t launch_idx(const void* x, int64_t rows, int64_t k, int64_t ld_x, uint8_t* q, uint8_t* sf,
                       float* ts, int dynamic, hipStream_t stream) {
   const int64_t total = rows * (k / 16);
-  const int64_t reach = total + (int64_t)kAmaxBlocksSmall * kMaxPartials * kThreads + 65536LL * kThreads;
+  const int64_t reach = total + (int64_t)kAmaxBlocks * kMaxPartials * kThreads +
+                        (int64_t)kQuantBlocks * 65536LL * kThreads;
   const char* force = getenv("MOE_FP4_INDEX64");
   const bool wide = force && force[0] == '1' && force[1] == '\0';
   if (reach < INT32_MAX && !wide)

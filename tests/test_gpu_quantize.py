@@ -142,12 +142,14 @@ def test_deterministic_and_stream_safe():
 
 # Dynamic scale: the amax launch hands its per-workgroup values to the quantise
 # launch inside q itself, one 2 KB piece (256 blocks) per quantise workgroup, with
-# at most 2048 pieces and 512 partial values.  These sizes sit on either side of
-# one piece, of the piece limit and of the partial limit, with the matrix's
-# largest element in its last block, which the grid-stride passes after the
-# first piece reach.
+# at most 512 pieces and 256 partial values (8 blocks per amax thread, 4 per
+# quantise thread and pass).  These sizes sit on either side of one piece, of
+# the piece limit (512 x 4096) and of the partial limit (1024 x 8192 and up),
+# with the matrix's largest element in its last block, which the grid-stride
+# passes after the first piece reach.
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("rows,k", [(1, 4080), (1, 4096), (1, 4112), (2, 4096),
+                                    (511, 4096), (512, 4096), (513, 4096),
                                     (1024, 8192), (1025, 8192), (4099, 6144)])
 def test_dynamic_scale_piece_boundaries(rows, k, dtype):
     rng = np.random.default_rng(rows * 7 + k)
