@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_fp4.so")
 SOURCES = ["api.cpp", "quantize.hip", "grouped_gemm.hip", "grouped_gemm_finalize.hip",
-           "grouped_gemm_swiglu.hip", "grouped_gemm_tiled.hip", "grouped_gemm_big.hip", "pack.hip", "combine.hip"]
+           "grouped_gemm_swiglu.hip", "grouped_gemm_tiled.hip", "grouped_gemm_big.hip", "grouped_gemm_mid.hip", "pack.hip", "combine.hip"]
 HEADERS = ["fp4_device.h", "gemm_common.h", "grouped_gemm_kernel.h", "launch.h"]
 
 HIPCC_FLAGS = [

@@ -77,6 +77,14 @@ GemmTile choose_tile(int32_t num_experts, int64_t m_total, int64_t n, int64_t k,
     }
     if (all || f8) return t;
   }
+  // Splits by expert size: "256x256m" (large tile from kBigRows rows, 64 x 256
+  // items below), "64x256p" (64 x 256 items from kMidRows rows, per-wave items
+  // below), "256x256mp" (all three).
+  if (env && k % 512 == 0 && mid_lds(num_experts) <= kLdsBytes && big_lds(num_experts) <= kLdsBytes) {
+    if (std::strcmp(env, "256x256m") == 0) return GemmTile{16, 16, 8, 1, 0, 5};
+    if (std::strcmp(env, "64x256p") == 0) return GemmTile{4, 16, 4, 2, 0, 6};
+    if (std::strcmp(env, "256x256mp") == 0) return GemmTile{16, 16, 8, 1, 0, 7};
+  }
   if (env && *env) {
     // "MxN" or "MxNxK", optionally followed by 'r' (weight scales through
     // registers rather than LDS): M rows per item, N columns per wave, K
@@ -97,6 +105,10 @@ GemmTile choose_tile(int32_t num_experts, int64_t m_total, int64_t n, int64_t k,
     ok = ok && *s == '\0' && nv >= 2;
     if (ok && nv == 2 && v[0] == 128 && v[1] == 128 && !regs) {
       t = GemmTile{8, 8, 4, 1, 0, 1};
+      return t;
+    }
+    if (ok && nv == 2 && v[0] == 64 && v[1] == 256 && !regs) {
+      if (k % 512 == 0 && mid_lds(num_experts) <= kLdsBytes) t = GemmTile{4, 16, 4, 2, 0, 4};
       return t;
     }
     if (ok && nv == 2 && v[0] == 256 && v[1] == 256 && !regs) {
@@ -121,6 +133,7 @@ GemmTile choose_tile(int32_t num_experts, int64_t m_total, int64_t n, int64_t k,
 }
 
 int32_t item_rows(const GemmTile& t) {
+  if (t.tiled == 4 || t.tiled == 6) return 64;
   if (t.tiled >= 2) return 256;
   if (t.tiled) return 128;
   return 16 * t.m_blocks;
@@ -138,7 +151,14 @@ void log_tile(const char* entry, int32_t num_experts, int64_t m_total, int64_t n
   static std::mutex mu;
   static std::string last;
   char line[320];
-  const char* kind = t.tiled == 3 ? (t.f8 ? "256x256 workgroup tile (FP8 split-K) for every expert"
+  const char* kind = t.tiled == 7 ? "256x256 workgroup tile for experts of >= 96 rows, 64x256 "
+                                    "workgroup items for 17-95 rows, 16x64 per-wave items below"
+                     : t.tiled == 6 ? "64x256 workgroup items for experts of >= 17 rows, 16x64 "
+                                      "per-wave items below"
+                     : t.tiled == 5 ? "256x256 workgroup tile for experts of >= 96 rows, 64x256 "
+                                      "workgroup items for the rest"
+                     : t.tiled == 4 ? "64x256 workgroup items for every expert"
+                     : t.tiled == 3 ? (t.f8 ? "256x256 workgroup tile (FP8 split-K) for every expert"
                                            : "256x256 workgroup tile for every expert")
                      : t.tiled == 2 ? (t.f8 ? "256x256 workgroup tile (FP8 split-K) for experts of "
                                               ">= 96 rows, 16x64 per-wave items for the rest"
@@ -150,7 +170,8 @@ void log_tile(const char* entry, int32_t num_experts, int64_t m_total, int64_t n
            "weight scales %s)\n",
            entry, (int)num_experts, (long long)m_total, (long long)n, (long long)k, (long long)ldo,
            kind, item_rows(t), t.tiled >= 2 ? 256 : t.tiled ? 128 : 16 * t.n_blocks,
-           t.tiled ? 64 : 256 * t.k_sub, t.tiled ? "in LDS stages" : t.lds_scales ? "via LDS lines" : "in registers");
+           t.tiled == 4 ? 256 : t.tiled ? 64 : 256 * t.k_sub,
+           t.tiled == 4 ? "in registers" : t.tiled ? "in LDS stages" : t.lds_scales ? "via LDS lines" : "in registers");
   std::lock_guard<std::mutex> g(mu);
   if (last == line) return;
   last = line;
@@ -158,6 +179,7 @@ void log_tile(const char* entry, int32_t num_experts, int64_t m_total, int64_t n
 }
 
 int64_t gemm_lds_bytes(const GemmTile& t, int32_t num_experts) {
+  if (t.tiled == 4 || t.tiled == 6) return (int64_t)mid_lds(num_experts) + 16;
   if (t.tiled >= 2) return (int64_t)big_lds(num_experts) + 16;
   if (t.tiled) return (int64_t)tiled_lds(num_experts) + 16;
   int64_t b = (int64_t)worklist_bytes(num_experts) + (int64_t)sizeof(int32_t) * t.waves;
@@ -216,6 +238,31 @@ GemmTile small_expert_tile(int64_t k) {
 }
 
 hipError_t launch_grouped_gemm(const GemmArgs& p, const GemmTile& t, hipStream_t stream) {
+  if (t.tiled == 4) return launch_grouped_gemm_mid(p, stream);
+  if (t.tiled >= 5) {
+    // Launches over disjoint expert-size ranges: the large tile from kBigRows
+    // rows (5, 7), 64 x 256 items in between, per-wave items below kMidRows (6, 7).
+    const bool use_big = t.tiled != 6, use_pw = t.tiled != 5;
+    hipError_t err = hipSuccess;
+    if (use_big) {
+      GemmArgs big = p;
+      big.rows_lo = kBigRows;
+      big.n_tiles = (int32_t)((p.n + 255) / 256);
+      err = launch_grouped_gemm_big(big, false, stream);
+      if (err != hipSuccess) return err;
+    }
+    GemmArgs mid = p;
+    mid.rows_lo = use_pw ? kMidRows : 0;
+    mid.rows_hi = use_big ? kBigRows : 0;
+    mid.n_tiles = (int32_t)((p.n + 255) / 256);
+    err = launch_grouped_gemm_mid(mid, stream);
+    if (err != hipSuccess || !use_pw) return err;
+    GemmArgs small = p;
+    const GemmTile s = small_expert_tile(p.k);
+    small.rows_hi = kMidRows;
+    small.n_tiles = (int32_t)((p.n + 16 * s.n_blocks - 1) / (16 * s.n_blocks));
+    return s.lds_scales ? launch_sl<true>(small, s, stream) : launch_sl<false>(small, s, stream);
+  }
   if (t.tiled == 3) return launch_grouped_gemm_big(p, t.f8 != 0, stream);
   if (t.tiled == 2) {
     // Experts with kBigRows rows or more in 256 x 256 items, the rest per wave.

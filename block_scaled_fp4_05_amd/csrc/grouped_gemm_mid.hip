@@ -1,0 +1,353 @@
+// NVFP4 grouped GEMM for gfx950, workgroup items for experts of a few dozen
+// rows: the prefill end of a skewed routing, where an expert owns more rows
+// than one 16-row block but far fewer than the 256 that make the large tile
+// pay ("Peering into the CUTLASS Kernel", section "Input Knowledge Required",
+// item 4: one GEMM per expert over its routed rows; "Peering into the CUTLASS
+// Kernel Scheduler", section "The Context": tile geometry decides the reuse at
+// small per-expert M).
+//
+// The per-wave kernel dequantises its 64 weight rows once per 16-row item, so
+// an expert of 48 rows converts every weight code three times, and the vector
+// ALU, not HBM, bounds it.  Here a workgroup of 4 wavefronts takes an item of
+// up to 64 rows x 256 columns and converts each operand once:
+//  * activations: per 256-element K stage the item's rows are dequantised
+//    exactly to FP16 by the whole workgroup (one thread per row and 64-element
+//    run) into one of two LDS buffers, and every wave reads its MFMA operands
+//    from there;
+//  * weights: each wave streams its own 64 weight rows (4 blocks of 16) into a
+//    two-stage register ring, as the per-wave kernel does, dequantises each
+//    fragment once and uses it for every 16-row block of the item.
+// Products run on v_mfma_f32_16x16x32_f16 (weights as the A operand, 16 output
+// columns; activations as B, 16 rows) with FP32 accumulation, and the tile
+// leaves through LDS in 16-byte stores of whole row segments.  Row blocks past
+// the item's rows issue no MFMAs (the K loop is instantiated per live block
+// count).  One barrier per stage orders the LDS traffic.
+//
+// K order: a stage is half of a 512-element granule (the packed weight
+// layout's unit), and lane group g of a wave owns elements 128 g + 64 s ..
+// +63 of granule half s, for weights and activations alike, so each product
+// pairs the same element and packed and row-major weights give identical
+// results.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp4_device.h"
+#include "gemm_common.h"
+#include "launch.h"
+
+namespace moe_fp4 {
+namespace {
+
+constexpr int kMThreads = 256;  // 4 wavefronts
+constexpr int kMCols = 256;     // output columns per item, 64 per wavefront
+constexpr int kMK = 256;        // K elements per stage
+constexpr int kMRow = 2 * kMK;  // bytes of one activation row of a stage in FP16
+// LDS pitch of a stage row: 16 bytes of padding put the 16 rows one 16-byte
+// access touches (same chunk, consecutive rows) in distinct banks, and every
+// per-step and per-block position stays an immediate offset.
+constexpr int kMPitch = kMRow + 16;
+constexpr int kMGranule = 512;  // K elements per granule (two stages)
+
+template <int MB>
+__host__ __device__ constexpr size_t mid_stage_bytes() {
+  return (size_t)16 * MB * kMPitch;
+}
+template <int MB>
+__host__ __device__ constexpr size_t mid_lds_bytes(int num_experts) {
+  return worklist_bytes(num_experts) + 2 * mid_stage_bytes<MB>();
+}
+
+// One stage of raw loads: a wave's 4 weight row blocks (the lane's 64 codes of
+// each, and their 4 block scales), and the loader thread's 64 activation
+// codes and 4 scales.
+struct MidStage {
+  u32x4_t w[4][2];
+  uint32_t ws[4];
+  u32x4_t a[2];
+  uint32_t as;
+};
+
+// Per-item buffer resources and lane offsets (bytes), fixed for the item; the
+// stage position goes in the scalar offset.
+struct MidLoads {
+  rsrc_t w, ws;
+  uint32_t wq[4], wsc[4];  // weight codes and scales, per row block
+  uint32_t aq, asc;        // loader thread's activation codes and scales
+  int32_t wk;              // packed: bytes of one granule of the wave's 64-row group
+};
+
+// Issue stage st's loads into `s`.  Past the last stage (`past`) every offset
+// is pushed out of range, so the loads return zeros without memory traffic
+// and every issue stays unconditional.  Activations go first: the end of the
+// previous stage waits for them alone.
+template <bool PK, int SUB>
+__device__ __forceinline__ void mid_issue(MidStage& s, const MidLoads& l, const rsrc_t& a_rs,
+                                          const rsrc_t& as_rs, int32_t granule, bool past) {
+  const uint32_t kill = past ? kOutOfRange : 0u;
+  const int32_t q = uniform(granule * (kMGranule / 2) + 32 * SUB);
+  const int32_t sc = uniform(granule * (kMGranule / 16) + 4 * SUB);
+  s.a[0] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, l.aq | kill, q, 0);
+  s.a[1] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, (l.aq + 16u) | kill, q, 0);
+  s.as = __builtin_amdgcn_raw_buffer_load_b32(as_rs, l.asc | kill, sc, 0);
+  // Packed: granule t of block j is 4 KB, its halves s 2 KB apart and the two
+  // 16-byte pieces of a lane 1 KB apart (one load of the wave reads 1 KB).
+  const int32_t qw = PK ? uniform(granule * l.wk + 2048 * SUB) : q;
+  constexpr uint32_t kHalf = PK ? 1024u : 16u;
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) {
+    s.w[jb][0] = __builtin_amdgcn_raw_buffer_load_b128(l.w, l.wq[jb] | kill, qw, 0);
+    s.w[jb][1] = __builtin_amdgcn_raw_buffer_load_b128(l.w, (l.wq[jb] + kHalf) | kill, qw, 0);
+    s.ws[jb] = __builtin_amdgcn_raw_buffer_load_b32(l.ws, l.wsc[jb] | kill, sc, 0);
+  }
+}
+
+// The loader thread's 64 activation values of a stage, dequantised exactly to
+// FP16 into LDS row `ar` of `buf`: 16-byte chunk q = 8 ag + w holds values
+// 8w .. 8w+7 of lane group ag's run.
+__device__ __forceinline__ void mid_put_act(uint8_t* buf, int ar, int ag, const MidStage& s) {
+  const half2_t lo = scale_pair_x2m8<false>(s.as), hi = scale_pair_x2m8<true>(s.as);
+  uint8_t* run = buf + ar * kMPitch + 128 * ag;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    const _Float16 sc = (w < 4 ? lo : hi)[(w >> 1) & 1];
+    const half8_t v = dequant8(w < 4 ? s.a[0][w & 3] : s.a[1][w & 3], sc);
+    *reinterpret_cast<half8_t*>(run + 16 * w) = v;
+  }
+}
+
+// The MFMAs of one stage for a wave: per 32-element step t, lane (c, g) reads
+// activation row 16 ib + c, values 8t .. 8t+7 of lane group g's run, for the
+// LIVE row blocks, and dequantises its weight fragment of each row block jb
+// once for all of them.
+template <int MB, int LIVE>
+__device__ __forceinline__ void mid_compute(const MidStage& s, const uint8_t* buf, int c, int g,
+                                            float4_t (&acc)[4][MB]) {
+  half2_t wsc[4][2];
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) {
+    wsc[jb][0] = scale_pair_x2m8<false>(s.ws[jb]);
+    wsc[jb][1] = scale_pair_x2m8<true>(s.ws[jb]);
+  }
+  const uint8_t* rbase = buf + c * kMPitch + 128 * g;
+  // Step t + 1's activation reads are issued before step t's MFMAs; the
+  // scheduling fence after each step keeps the compiler from hoisting every
+  // read of the stage at once (which would not fit the registers).
+  half8_t af[2][LIVE];
+  auto read_af = [&](half8_t (&dst)[LIVE], int t) {
+#pragma unroll
+    for (int ib = 0; ib < LIVE; ++ib)
+      dst[ib] = *reinterpret_cast<const half8_t*>(rbase + 16 * ib * kMPitch + 16 * t);
+  };
+  read_af(af[0], 0);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    if (t < 7) read_af(af[(t + 1) & 1], t + 1);
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+      const half8_t wf = dequant8(s.w[jb][t >> 2][t & 3], wsc[jb][t >> 2][(t >> 1) & 1]);
+#pragma unroll
+      for (int ib = 0; ib < LIVE; ++ib)
+        acc[jb][ib] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf, af[t & 1][ib], acc[jb][ib], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// The K loop of one item with LIVE row blocks: stage st computes from ring
+// slot st % 2 and LDS buffer st % 2, then writes stage st+1's activations
+// into the other buffer, reloads its slot with stage st+2 and meets the
+// workgroup at the barrier.  The caller has issued stages 0 and 1 and filled
+// buffer 0.  The stage count is even (K is a multiple of 512).
+template <int MB, int LIVE, bool PK>
+__device__ __forceinline__ void mid_k_loop(float4_t (&acc)[4][MB], MidStage (&ring)[2],
+                                           const MidLoads& l, const rsrc_t& a_rs,
+                                           const rsrc_t& as_rs, uint8_t* stages, int32_t ngr,
+                                           bool loader, int ar, int ag, int c, int g) {
+  uint8_t* const buf0 = stages;
+  uint8_t* const buf1 = stages + mid_stage_bytes<MB>();
+  for (int32_t gr = 0; gr < ngr; ++gr) {
+    // Stage 2 gr: slot 0, buffer 0.
+    mid_compute<MB, LIVE>(ring[0], buf0, c, g, acc);
+    if (loader) mid_put_act(buf1, ar, ag, ring[1]);
+    mid_issue<PK, 0>(ring[0], l, a_rs, as_rs, gr + 1, gr + 1 >= ngr);
+    __syncthreads();
+    // Stage 2 gr + 1: slot 1, buffer 1.
+    mid_compute<MB, LIVE>(ring[1], buf1, c, g, acc);
+    if (loader && gr + 1 < ngr) mid_put_act(buf0, ar, ag, ring[0]);
+    mid_issue<PK, 1>(ring[1], l, a_rs, as_rs, gr + 1, gr + 1 >= ngr);
+    __syncthreads();
+  }
+}
+
+// BF16 epilogue of an item through LDS (`tile`: 16 MB rows of 512 bytes, free
+// after the K loop's last barrier).  Lane (c, g) of wave wv holds, for row
+// 16 ib + c, columns 64 wv + 16 jb + 4 g .. +3; those 8 bytes go to 16-byte
+// chunk 8 wv + 2 jb + g / 2 of the row (position chunk ^ (row % 32)).  The
+// workgroup then stores 16-byte chunks of whole rows.  Rows past the
+// expert's end fall outside the store resource; chunks past n get an
+// out-of-range offset.  Ends with a barrier (the next item rewrites `tile`).
+template <int MB>
+__device__ __forceinline__ void mid_store(float4_t (&acc)[4][MB], const ItemPos& it,
+                                          const GemmArgs& p, uint8_t* tile, int tid, int wave,
+                                          int c, int g) {
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) {
+#pragma unroll
+    for (int ib = 0; ib < MB; ++ib) {
+      const float4_t v = acc[jb][ib];
+      const bf16x4_t b = {(__bf16)(v[0] * it.alpha), (__bf16)(v[1] * it.alpha),
+                          (__bf16)(v[2] * it.alpha), (__bf16)(v[3] * it.alpha)};
+      const int row = 16 * ib + c, chunk = 8 * wave + 2 * jb + (g >> 1);
+      *reinterpret_cast<u32x2_t*>(tile + row * kMRow + 16 * (chunk ^ (row & 31)) + 8 * (g & 1)) =
+          __builtin_bit_cast(u32x2_t, b);
+    }
+  }
+  __syncthreads();
+  // The host picks this kernel only when 64 rows of ldo BF16 values stay below
+  // 2^31 - 4096 bytes, so the resource size and every offset fit 31 bits.
+  const uint32_t ldo = (uint32_t)p.ldo;
+  const rsrc_t o = make_rsrc(p.out + (int64_t)it.row0 * ldo, (uint32_t)it.rows_valid * ldo * 2u);
+  const int chunk = tid & 31, r0 = tid >> 5;  // 8 rows per pass of the workgroup
+  const bool col_ok = it.n0 + 8 * chunk < (int32_t)p.n;
+#pragma unroll
+  for (int i = 0; i < 2 * MB; ++i) {
+    const int row = r0 + 8 * i;
+    const u32x4_t d = *reinterpret_cast<const u32x4_t*>(tile + row * kMRow + 16 * (chunk ^ (row & 31)));
+    const uint32_t off = col_ok ? ((uint32_t)row * ldo + (uint32_t)(it.n0 + 8 * chunk)) * 2u : kOutOfRange;
+    __builtin_amdgcn_raw_buffer_store_b128(d, o, off, 0, 0);
+  }
+  __syncthreads();
+}
+
+// One item with LIVE row blocks: lane offsets, the first two stages, the K
+// loop and the epilogue.  Instantiated per LIVE, with every register the item
+// needs declared inside, so the branches of the caller's switch share none.
+template <int MB, int LIVE, bool PK>
+__device__ __forceinline__ void mid_item(const GemmArgs& p, const ItemPos& it, uint8_t* stages,
+                                         const rsrc_t& a_rs, const rsrc_t& as_rs, int tid,
+                                         int wave, bool loader, int ar, int ag) {
+  const int lane = tid & 63, c = lane & 15, g = lane >> 4;
+  // 32-bit offsets: the host guarantees n * k/2 and a_rows * k/2 < 2^31.
+  const int32_t n = (int32_t)p.n, kb = (int32_t)(p.k >> 1), nbk = (int32_t)(p.k >> 4);
+  const int32_t ngr = (int32_t)(p.k / kMGranule);
+  const int32_t a_last = (int32_t)p.a_rows - 1;
+  MidLoads l;
+  l.w = make_rsrc(p.w_q + (int64_t)it.e * n * kb, (uint32_t)(n * kb));
+  l.ws = make_rsrc(p.w_sf + (int64_t)it.e * n * nbk, (uint32_t)(n * nbk));
+  const int32_t grp0 = uniform(it.n0 + 64 * wave);  // this wave's 64 weight rows
+  {
+    const int32_t left = grp0 < n ? (n - grp0) >> 4 : 0;
+    l.wk = uniform((left < 4 ? left : 4) * packed_block_bytes(kMGranule));
+  }
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) {
+    const int32_t row = grp0 + 16 * jb + c;
+    const bool ok = row < n;
+    const uint32_t wv = PK ? (uint32_t)(grp0 * kb + jb * packed_block_bytes(kMGranule) + 16 * lane)
+                           : (uint32_t)(row * kb + (kMGranule / 8) * g);
+    l.wq[jb] = ok ? wv : kOutOfRange;
+    l.wsc[jb] = ok ? (uint32_t)(row * nbk + (kMGranule / 64) * g) : kOutOfRange;
+  }
+  {
+    // Rows past the expert's end load nothing (zeros): their products are
+    // computed in a partly live row block and never stored.
+    const bool a_ok = loader && ar < it.rows_valid;
+    int32_t src = it.row0 + (a_ok ? ar : 0);
+    if (p.a_row_index) src = p.a_row_index[src];
+    src = src < 0 ? 0 : (src > a_last ? a_last : src);
+    l.aq = a_ok ? (uint32_t)(src * kb + (kMGranule / 8) * ag) : kOutOfRange;
+    l.asc = a_ok ? (uint32_t)(src * nbk + (kMGranule / 64) * ag) : kOutOfRange;
+  }
+
+  float4_t acc[4][MB];
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+    for (int ib = 0; ib < MB; ++ib) acc[jb][ib] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  MidStage ring[2];
+  mid_issue<PK, 0>(ring[0], l, a_rs, as_rs, 0, false);
+  mid_issue<PK, 1>(ring[1], l, a_rs, as_rs, 0, false);
+  if (loader) mid_put_act(stages, ar, ag, ring[0]);
+  __syncthreads();
+  mid_k_loop<MB, LIVE, PK>(acc, ring, l, a_rs, as_rs, stages, ngr, loader, ar, ag, c, g);
+  mid_store<MB>(acc, it, p, stages, tid, wave, c, g);
+}
+
+template <int MB, bool PK>
+__global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_grouped_gemm_mid(const GemmArgs p) {
+  constexpr int BM = 16 * MB;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  int32_t* prefix = reinterpret_cast<int32_t*>(smem);
+  int32_t* offl = prefix + (p.num_experts + 1);
+  __shared__ int32_t wave_sum[kMThreads / 64];
+  uint8_t* const stages = smem + worklist_bytes(p.num_experts);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  // Activation loader role: thread (ar, ag) converts row ar, lane group ag's
+  // run; 16 consecutive lanes take 16 consecutive rows of one run.
+  const int ar = tid % BM, ag = tid / BM;
+  const bool loader = tid < 4 * BM;
+
+  const int32_t total_items = build_worklist<kMThreads>(p, BM, prefix, offl, wave_sum);
+  const WorkList wl{prefix, offl};
+
+  const int nblk = gridDim.x, b = blockIdx.x;
+  const int32_t rounds = (total_items + nblk - 1) / nblk;
+  if (rounds == 0) return;
+  const int32_t last_items = total_items - (rounds - 1) * nblk;
+  const int32_t lb_full = logical_block(b, nblk, nblk);
+  const int32_t lb_last = logical_block(b, nblk, last_items);
+  const int32_t my_items = (rounds - 1) + (lb_last < last_items ? 1 : 0);
+
+  const rsrc_t a_rs = make_rsrc(p.a_q, (uint32_t)(p.a_rows * (p.k >> 1)));
+  const rsrc_t as_rs = make_rsrc(p.a_sf, (uint32_t)(p.a_rows * (p.k >> 4)));
+
+  int32_t from = 0;
+  for (int32_t j = 0; j < my_items; ++j) {
+    const int32_t item = j * nblk + (j == rounds - 1 ? lb_last : lb_full);
+    const ItemPos it = locate(item, from, wl, p, BM, kMCols, lane);
+    from = it.e;
+    const int live = (it.rows_valid + 15) >> 4;
+    if (live == 1) {
+      mid_item<MB, 1, PK>(p, it, stages, a_rs, as_rs, tid, wave, loader, ar, ag);
+    } else if (MB >= 2 && live == 2) {
+      mid_item<MB, (MB >= 2 ? 2 : 1), PK>(p, it, stages, a_rs, as_rs, tid, wave, loader, ar, ag);
+    } else if (MB >= 3 && live == 3) {
+      mid_item<MB, (MB >= 3 ? 3 : 1), PK>(p, it, stages, a_rs, as_rs, tid, wave, loader, ar, ag);
+    } else {
+      mid_item<MB, MB, PK>(p, it, stages, a_rs, as_rs, tid, wave, loader, ar, ag);
+    }
+  }
+}
+
+constexpr int kMidBlocks = 4;  // 64-row items
+
+}  // namespace
+
+size_t mid_lds(int32_t num_experts) { return mid_lds_bytes<kMidBlocks>(num_experts); }
+
+hipError_t launch_grouped_gemm_mid(const GemmArgs& p, hipStream_t stream) {
+  if (p.k % kMGranule != 0) return hipErrorInvalidValue;
+  auto kern = p.w_packed ? k_grouped_gemm_mid<kMidBlocks, true> : k_grouped_gemm_mid<kMidBlocks, false>;
+  const size_t lds = mid_lds_bytes<kMidBlocks>(p.num_experts);
+  if (lds > kLdsBytes) return hipErrorInvalidValue;  // the host picks this tile only if it fits
+  int resident = 0;
+  hipError_t err = resident_groups(kern, kMThreads, lds, &resident);
+  if (err != hipSuccess) return err;
+  // Upper bound on the number of items: the host does not see the offsets.
+  constexpr int BM = 16 * kMidBlocks;
+  const int64_t max_mtiles = p.m_total / BM + (p.m_total < p.num_experts ? p.m_total : p.num_experts);
+  const int64_t max_items = max_mtiles * p.n_tiles;
+  int64_t grid = resident;
+  if (max_items < grid) grid = max_items;
+  if (grid < 1) grid = 1;
+  grid = (grid + kXcds - 1) / kXcds * kXcds;  // whole rounds over the XCDs
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kMThreads), lds, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace moe_fp4
