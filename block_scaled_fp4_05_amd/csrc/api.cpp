@@ -123,7 +123,7 @@ int moe_grouped_gemm_fp4_plan(int32_t num_experts, int64_t m_total, int64_t n, i
   const GemmTile t = moe_fp4::choose_tile(num_experts, m_total, n, k, getenv("MOE_FP4_TILE"));
   plan->tile_m = 16 * t.m_blocks;
   plan->tile_n = 16 * t.n_blocks;
-  plan->k_step = t.tiled == 4 ? 256 : t.tiled ? 64 : moe_fp4::kKStep * t.k_sub;
+  plan->k_step = (t.tiled == 4 || t.tiled == 6) ? 256 : t.tiled ? 64 : moe_fp4::kKStep * t.k_sub;
   plan->waves_per_group = t.waves;
   plan->lds_bytes = moe_fp4::gemm_lds_bytes(t, num_experts);
   return MOE_FP4_OK;

@@ -54,14 +54,20 @@ GemmTile choose_tile(int32_t num_experts, int64_t m_total, int64_t n, int64_t k,
   else if (avg > 16) t.m_blocks = 2;
   // Experts this large are compute-bound: share dequantised operands in LDS.
   // When the work list leaves room for two 64 KB stages, experts with at least
-  // kBigRows rows take 256 x 256 items and the rest the per-wave kernel (two
-  // launches over disjoint experts, chosen on the device from the offsets);
-  // else every expert takes 128 x 128 items.
-  // A single expert takes the large tile in one launch (the per-wave launch of
-  // the split would find no expert to run and still cost its few microseconds).
-  if (avg >= 96) t = big_lds(num_experts) <= kLdsBytes
-                         ? GemmTile{16, 16, 8, 1, 0, num_experts == 1 ? 3 : 2}
-                         : GemmTile{8, 8, 4, 1, 0, 1};
+  // kBigRows rows take 256 x 256 items and the rest 48 x 256 items (K a
+  // multiple of 512) or per-wave items (two launches over disjoint experts,
+  // chosen on the device from the offsets); else every expert takes 128 x 128
+  // items.  A single expert takes the large tile in one launch (the second
+  // launch of the split would find no expert to run and still cost its few
+  // microseconds).  Measured on the Zipf prefill shard (256 experts, 4096
+  // tokens top-8): 48 x 256 items for the experts below 96 rows 284-288 us,
+  // per-wave items 298-302 us.
+  if (avg >= 96) {
+    const bool mid = k % 512 == 0 && mid_lds(num_experts) <= kLdsBytes;
+    t = big_lds(num_experts) > kLdsBytes ? GemmTile{8, 8, 4, 1, 0, 1}
+        : num_experts == 1              ? GemmTile{16, 16, 8, 1, 0, 3}
+                                        : GemmTile{16, 16, 8, 1, 0, mid ? 5 : 2};
+  }
   if (k % 512 == 0) t.k_sub = 2;
   t.lds_scales = k % kSpan == 0 ? 1 : 0;
   // "256x256!": every expert in 256 x 256 items, however few its rows.
@@ -77,12 +83,12 @@ GemmTile choose_tile(int32_t num_experts, int64_t m_total, int64_t n, int64_t k,
     }
     if (all || f8) return t;
   }
-  // Splits by expert size: "256x256m" (large tile from kBigRows rows, 64 x 256
-  // items below), "64x256p" (64 x 256 items from kMidRows rows, per-wave items
+  // Splits by expert size: "256x256m" (large tile from kBigRows rows, 48 x 256
+  // items below), "48x256p" (48 x 256 items from kMidRows rows, per-wave items
   // below), "256x256mp" (all three).
   if (env && k % 512 == 0 && mid_lds(num_experts) <= kLdsBytes && big_lds(num_experts) <= kLdsBytes) {
     if (std::strcmp(env, "256x256m") == 0) return GemmTile{16, 16, 8, 1, 0, 5};
-    if (std::strcmp(env, "64x256p") == 0) return GemmTile{4, 16, 4, 2, 0, 6};
+    if (std::strcmp(env, "48x256p") == 0) return GemmTile{3, 16, 4, 2, 0, 6};
     if (std::strcmp(env, "256x256mp") == 0) return GemmTile{16, 16, 8, 1, 0, 7};
   }
   if (env && *env) {
@@ -107,8 +113,8 @@ GemmTile choose_tile(int32_t num_experts, int64_t m_total, int64_t n, int64_t k,
       t = GemmTile{8, 8, 4, 1, 0, 1};
       return t;
     }
-    if (ok && nv == 2 && v[0] == 64 && v[1] == 256 && !regs) {
-      if (k % 512 == 0 && mid_lds(num_experts) <= kLdsBytes) t = GemmTile{4, 16, 4, 2, 0, 4};
+    if (ok && nv == 2 && v[0] == 48 && v[1] == 256 && !regs) {
+      if (k % 512 == 0 && mid_lds(num_experts) <= kLdsBytes) t = GemmTile{3, 16, 4, 2, 0, 4};
       return t;
     }
     if (ok && nv == 2 && v[0] == 256 && v[1] == 256 && !regs) {
@@ -133,7 +139,7 @@ GemmTile choose_tile(int32_t num_experts, int64_t m_total, int64_t n, int64_t k,
 }
 
 int32_t item_rows(const GemmTile& t) {
-  if (t.tiled == 4 || t.tiled == 6) return 64;
+  if (t.tiled == 4 || t.tiled == 6) return 48;
   if (t.tiled >= 2) return 256;
   if (t.tiled) return 128;
   return 16 * t.m_blocks;
@@ -151,13 +157,13 @@ void log_tile(const char* entry, int32_t num_experts, int64_t m_total, int64_t n
   static std::mutex mu;
   static std::string last;
   char line[320];
-  const char* kind = t.tiled == 7 ? "256x256 workgroup tile for experts of >= 96 rows, 64x256 "
+  const char* kind = t.tiled == 7 ? "256x256 workgroup tile for experts of >= 96 rows, 48x256 "
                                     "workgroup items for 17-95 rows, 16x64 per-wave items below"
-                     : t.tiled == 6 ? "64x256 workgroup items for experts of >= 17 rows, 16x64 "
+                     : t.tiled == 6 ? "48x256 workgroup items for experts of >= 17 rows, 16x64 "
                                       "per-wave items below"
-                     : t.tiled == 5 ? "256x256 workgroup tile for experts of >= 96 rows, 64x256 "
+                     : t.tiled == 5 ? "256x256 workgroup tile for experts of >= 96 rows, 48x256 "
                                       "workgroup items for the rest"
-                     : t.tiled == 4 ? "64x256 workgroup items for every expert"
+                     : t.tiled == 4 ? "48x256 workgroup items for every expert"
                      : t.tiled == 3 ? (t.f8 ? "256x256 workgroup tile (FP8 split-K) for every expert"
                                            : "256x256 workgroup tile for every expert")
                      : t.tiled == 2 ? (t.f8 ? "256x256 workgroup tile (FP8 split-K) for experts of "
@@ -241,7 +247,7 @@ hipError_t launch_grouped_gemm(const GemmArgs& p, const GemmTile& t, hipStream_t
   if (t.tiled == 4) return launch_grouped_gemm_mid(p, stream);
   if (t.tiled >= 5) {
     // Launches over disjoint expert-size ranges: the large tile from kBigRows
-    // rows (5, 7), 64 x 256 items in between, per-wave items below kMidRows (6, 7).
+    // rows (5, 7), 48 x 256 items in between, per-wave items below kMidRows (6, 7).
     const bool use_big = t.tiled != 6, use_pw = t.tiled != 5;
     hipError_t err = hipSuccess;
     if (use_big) {

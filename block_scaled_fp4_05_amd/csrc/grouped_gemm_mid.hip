@@ -9,14 +9,15 @@
 // The per-wave kernel dequantises its 64 weight rows once per 16-row item, so
 // an expert of 48 rows converts every weight code three times, and the vector
 // ALU, not HBM, bounds it.  Here a workgroup of 4 wavefronts takes an item of
-// up to 64 rows x 256 columns and converts each operand once:
+// up to 48 rows x 256 columns and converts each operand once:
 //  * activations: per 256-element K stage the item's rows are dequantised
 //    exactly to FP16 by the whole workgroup (one thread per row and 64-element
 //    run) into one of two LDS buffers, and every wave reads its MFMA operands
 //    from there;
 //  * weights: each wave streams its own 64 weight rows (4 blocks of 16) into a
-//    two-stage register ring, as the per-wave kernel does, dequantises each
-//    fragment once and uses it for every 16-row block of the item.
+//    three-stage register ring (two stages in flight while one computes),
+//    dequantises each fragment once and uses it for every 16-row block of the
+//    item.
 // Products run on v_mfma_f32_16x16x32_f16 (weights as the A operand, 16 output
 // columns; activations as B, 16 rows) with FP32 accumulation, and the tile
 // leaves through LDS in 16-byte stores of whole row segments.  Row blocks past
@@ -30,6 +31,9 @@
 // results.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
+#include <utility>
 
 #include "fp4_device.h"
 #include "gemm_common.h"
@@ -153,29 +157,42 @@ __device__ __forceinline__ void mid_compute(const MidStage& s, const uint8_t* bu
   }
 }
 
-// The K loop of one item with LIVE row blocks: stage st computes from ring
-// slot st % 2 and LDS buffer st % 2, then writes stage st+1's activations
-// into the other buffer, reloads its slot with stage st+2 and meets the
-// workgroup at the barrier.  The caller has issued stages 0 and 1 and filled
-// buffer 0.  The stage count is even (K is a multiple of 512).
-template <int MB, int LIVE, bool PK>
-__device__ __forceinline__ void mid_k_loop(float4_t (&acc)[4][MB], MidStage (&ring)[2],
+// Calls f(integral_constant<int, 0>) .. f(integral_constant<int, N-1>), unrolled.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// The K loop of one item with LIVE row blocks and a ring of R register
+// stages: stage st computes from ring slot st % R and LDS buffer st % 2, then
+// writes stage st+1's activations (loaded R-1 stages earlier) into the other
+// buffer, reloads its slot with stage st+R and meets the workgroup at the
+// barrier, so R-1 stages of loads stay in flight while one computes.  The
+// caller has issued stages 0 .. R-1 and filled buffer 0.  Unrolled by a
+// multiple of R and 2, so every slot, buffer and granule half is a constant.
+template <int MB, int LIVE, bool PK, int R>
+__device__ __forceinline__ void mid_k_loop(float4_t (&acc)[4][MB], MidStage (&ring)[R],
                                            const MidLoads& l, const rsrc_t& a_rs,
-                                           const rsrc_t& as_rs, uint8_t* stages, int32_t ngr,
+                                           const rsrc_t& as_rs, uint8_t* stages, int32_t nst,
                                            bool loader, int ar, int ag, int c, int g) {
-  uint8_t* const buf0 = stages;
-  uint8_t* const buf1 = stages + mid_stage_bytes<MB>();
-  for (int32_t gr = 0; gr < ngr; ++gr) {
-    // Stage 2 gr: slot 0, buffer 0.
-    mid_compute<MB, LIVE>(ring[0], buf0, c, g, acc);
-    if (loader) mid_put_act(buf1, ar, ag, ring[1]);
-    mid_issue<PK, 0>(ring[0], l, a_rs, as_rs, gr + 1, gr + 1 >= ngr);
-    __syncthreads();
-    // Stage 2 gr + 1: slot 1, buffer 1.
-    mid_compute<MB, LIVE>(ring[1], buf1, c, g, acc);
-    if (loader && gr + 1 < ngr) mid_put_act(buf0, ar, ag, ring[0]);
-    mid_issue<PK, 1>(ring[1], l, a_rs, as_rs, gr + 1, gr + 1 >= ngr);
-    __syncthreads();
+  constexpr int U = R % 2 == 0 ? R : 2 * R;
+  uint8_t* const buf[2] = {stages, stages + mid_stage_bytes<MB>()};
+  for (int32_t st0 = 0; st0 < nst; st0 += U) {
+    static_for<U>([&](auto dd) {
+      constexpr int D = decltype(dd)::value;
+      const int32_t st = st0 + D;
+      if (D == 0 || st < nst) {
+        mid_compute<MB, LIVE>(ring[D % R], buf[D & 1], c, g, acc);
+        if (loader && st + 1 < nst) mid_put_act(buf[(D + 1) & 1], ar, ag, ring[(D + 1) % R]);
+        const int32_t nxt = st + R;  // st0 is even: nxt's granule half is (D + R) % 2
+        mid_issue<PK, (D + R) & 1>(ring[D % R], l, a_rs, as_rs, nxt >> 1, nxt >= nst);
+        __syncthreads();
+      }
+    });
   }
 }
 
@@ -204,7 +221,7 @@ __device__ __forceinline__ void mid_store(float4_t (&acc)[4][MB], const ItemPos&
     }
   }
   __syncthreads();
-  // The host picks this kernel only when 64 rows of ldo BF16 values stay below
+  // The host picks this kernel only when 48 rows of ldo BF16 values stay below
   // 2^31 - 4096 bytes, so the resource size and every offset fit 31 bits.
   const uint32_t ldo = (uint32_t)p.ldo;
   const rsrc_t o = make_rsrc(p.out + (int64_t)it.row0 * ldo, (uint32_t)it.rows_valid * ldo * 2u);
@@ -223,14 +240,14 @@ __device__ __forceinline__ void mid_store(float4_t (&acc)[4][MB], const ItemPos&
 // One item with LIVE row blocks: lane offsets, the first two stages, the K
 // loop and the epilogue.  Instantiated per LIVE, with every register the item
 // needs declared inside, so the branches of the caller's switch share none.
-template <int MB, int LIVE, bool PK>
+template <int MB, int LIVE, bool PK, int R>
 __device__ __forceinline__ void mid_item(const GemmArgs& p, const ItemPos& it, uint8_t* stages,
                                          const rsrc_t& a_rs, const rsrc_t& as_rs, int tid,
                                          int wave, bool loader, int ar, int ag) {
   const int lane = tid & 63, c = lane & 15, g = lane >> 4;
   // 32-bit offsets: the host guarantees n * k/2 and a_rows * k/2 < 2^31.
   const int32_t n = (int32_t)p.n, kb = (int32_t)(p.k >> 1), nbk = (int32_t)(p.k >> 4);
-  const int32_t ngr = (int32_t)(p.k / kMGranule);
+  const int32_t nst = (int32_t)(p.k / kMK);  // even: K is a multiple of 512
   const int32_t a_last = (int32_t)p.a_rows - 1;
   MidLoads l;
   l.w = make_rsrc(p.w_q + (int64_t)it.e * n * kb, (uint32_t)(n * kb));
@@ -266,16 +283,18 @@ __device__ __forceinline__ void mid_item(const GemmArgs& p, const ItemPos& it, u
 #pragma unroll
     for (int ib = 0; ib < MB; ++ib) acc[jb][ib] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  MidStage ring[2];
-  mid_issue<PK, 0>(ring[0], l, a_rs, as_rs, 0, false);
-  mid_issue<PK, 1>(ring[1], l, a_rs, as_rs, 0, false);
+  MidStage ring[R];
+  static_for<R>([&](auto dd) {
+    constexpr int D = decltype(dd)::value;
+    mid_issue<PK, D & 1>(ring[D], l, a_rs, as_rs, D >> 1, D >= nst);
+  });
   if (loader) mid_put_act(stages, ar, ag, ring[0]);
   __syncthreads();
-  mid_k_loop<MB, LIVE, PK>(acc, ring, l, a_rs, as_rs, stages, ngr, loader, ar, ag, c, g);
+  mid_k_loop<MB, LIVE, PK, R>(acc, ring, l, a_rs, as_rs, stages, nst, loader, ar, ag, c, g);
   mid_store<MB>(acc, it, p, stages, tid, wave, c, g);
 }
 
-template <int MB, bool PK>
+template <int MB, int R, bool PK>
 __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_grouped_gemm_mid(const GemmArgs p) {
   constexpr int BM = 16 * MB;
@@ -312,19 +331,22 @@ void k_grouped_gemm_mid(const GemmArgs p) {
     const ItemPos it = locate(item, from, wl, p, BM, kMCols, lane);
     from = it.e;
     const int live = (it.rows_valid + 15) >> 4;
-    if (live == 1) {
-      mid_item<MB, 1, PK>(p, it, stages, a_rs, as_rs, tid, wave, loader, ar, ag);
-    } else if (MB >= 2 && live == 2) {
-      mid_item<MB, (MB >= 2 ? 2 : 1), PK>(p, it, stages, a_rs, as_rs, tid, wave, loader, ar, ag);
-    } else if (MB >= 3 && live == 3) {
-      mid_item<MB, (MB >= 3 ? 3 : 1), PK>(p, it, stages, a_rs, as_rs, tid, wave, loader, ar, ag);
+    if (live <= 1) {
+      mid_item<MB, 1, PK, R>(p, it, stages, a_rs, as_rs, tid, wave, loader, ar, ag);
+    } else if (live == 2 && MB > 2) {
+      if constexpr (MB > 2) mid_item<MB, 2, PK, R>(p, it, stages, a_rs, as_rs, tid, wave, loader, ar, ag);
+    } else if (live == 3 && MB > 3) {
+      if constexpr (MB > 3) mid_item<MB, 3, PK, R>(p, it, stages, a_rs, as_rs, tid, wave, loader, ar, ag);
     } else {
-      mid_item<MB, MB, PK>(p, it, stages, a_rs, as_rs, tid, wave, loader, ar, ag);
+      mid_item<MB, MB, PK, R>(p, it, stages, a_rs, as_rs, tid, wave, loader, ar, ag);
     }
   }
 }
 
-constexpr int kMidBlocks = 4;  // 64-row items
+// 48-row items with three register stages (two in flight while one
+// computes): the in-flight bytes, not the arithmetic, bound this kernel.
+constexpr int kMidBlocks = 3;
+constexpr int kMidRing = 3;
 
 }  // namespace
 
@@ -332,7 +354,8 @@ size_t mid_lds(int32_t num_experts) { return mid_lds_bytes<kMidBlocks>(num_exper
 
 hipError_t launch_grouped_gemm_mid(const GemmArgs& p, hipStream_t stream) {
   if (p.k % kMGranule != 0) return hipErrorInvalidValue;
-  auto kern = p.w_packed ? k_grouped_gemm_mid<kMidBlocks, true> : k_grouped_gemm_mid<kMidBlocks, false>;
+  auto kern = p.w_packed ? k_grouped_gemm_mid<kMidBlocks, kMidRing, true>
+                        : k_grouped_gemm_mid<kMidBlocks, kMidRing, false>;
   const size_t lds = mid_lds_bytes<kMidBlocks>(p.num_experts);
   if (lds > kLdsBytes) return hipErrorInvalidValue;  // the host picks this tile only if it fits
   int resident = 0;

@@ -388,7 +388,17 @@ typedef struct {
  * for these sizes (m_total / num_experts rows per expert on average).
  * Returns MOE_FP4_OK, or NULL / SHAPE / UNSUPPORTED as the GEMM would.
  * The MOE_FP4_TILE environment variable ("MxN", e.g. "32x64") overrides the
- * choice of tile_m x tile_n when it names a supported tile.
+ * choice of tile_m x tile_n when it names a supported tile: per-wave items
+ * "16x64", "32x64", "64x64", "16x32", "32x32", "64x32" (optionally "xK" with K
+ * 256, 512 or 1024 elements per stage, and "r" to keep the weight scales in
+ * registers); workgroup items "128x128", "256x256" (experts of 96 rows or more;
+ * per-wave items for the rest), "256x256!" (every expert), "256x256f8" and
+ * "256x256f8!" (the same with K split by scale block on the FP8 MFMA),
+ * "48x256" (every expert), and the splits by expert size "256x256m" (256 x 256
+ * from 96 rows, 48 x 256 below: the default when experts average 96 rows or
+ * more and K is a multiple of 512), "48x256p" (48 x 256 from 17 rows, per-wave
+ * items below) and "256x256mp" (all three).  The 48 x 256 items need K to be a
+ * multiple of 512; asked for otherwise, the default choice stands.
  */
 int moe_grouped_gemm_fp4_plan(int32_t num_experts, int64_t m_total, int64_t n, int64_t k,
                               moe_fp4_gemm_plan* plan);
