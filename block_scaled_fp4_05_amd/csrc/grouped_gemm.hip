@@ -54,13 +54,13 @@ GemmTile choose_tile(int32_t num_experts, int64_t m_total, int64_t n, int64_t k,
   else if (avg > 16) t.m_blocks = 2;
   // Experts this large are compute-bound: share dequantised operands in LDS.
   // When the work list leaves room for two 64 KB stages, experts with at least
-  // kBigRows rows take 256 x 256 items and the rest 48 x 256 items (K a
+  // kBigRows rows take 256 x 256 items and the rest 48 x 512 items (K a
   // multiple of 512) or per-wave items (two launches over disjoint experts,
   // chosen on the device from the offsets); else every expert takes 128 x 128
   // items.  A single expert takes the large tile in one launch (the second
   // launch of the split would find no expert to run and still cost its few
   // microseconds).  Measured on the Zipf prefill shard (256 experts, 4096
-  // tokens top-8): 48 x 256 items for the experts below 96 rows 284-288 us,
+  // tokens top-8): 48 x 512 items for the experts below 96 rows 284-288 us,
   // per-wave items 298-302 us.
   if (avg >= 96) {
     const bool mid = k % 512 == 0 && mid_lds(num_experts) <= kLdsBytes;
@@ -83,12 +83,12 @@ GemmTile choose_tile(int32_t num_experts, int64_t m_total, int64_t n, int64_t k,
     }
     if (all || f8) return t;
   }
-  // Splits by expert size: "256x256m" (large tile from kBigRows rows, 48 x 256
-  // items below), "48x256p" (48 x 256 items from kMidRows rows, per-wave items
+  // Splits by expert size: "256x256m" (large tile from kBigRows rows, 48 x 512
+  // items below), "48x512p" (48 x 512 items from kMidRows rows, per-wave items
   // below), "256x256mp" (all three).
   if (env && k % 512 == 0 && mid_lds(num_experts) <= kLdsBytes && big_lds(num_experts) <= kLdsBytes) {
     if (std::strcmp(env, "256x256m") == 0) return GemmTile{16, 16, 8, 1, 0, 5};
-    if (std::strcmp(env, "48x256p") == 0) return GemmTile{3, 16, 4, 2, 0, 6};
+    if (std::strcmp(env, "48x512p") == 0) return GemmTile{3, 32, 8, 2, 0, 6};
     if (std::strcmp(env, "256x256mp") == 0) return GemmTile{16, 16, 8, 1, 0, 7};
   }
   if (env && *env) {
@@ -113,8 +113,8 @@ GemmTile choose_tile(int32_t num_experts, int64_t m_total, int64_t n, int64_t k,
       t = GemmTile{8, 8, 4, 1, 0, 1};
       return t;
     }
-    if (ok && nv == 2 && v[0] == 48 && v[1] == 256 && !regs) {
-      if (k % 512 == 0 && mid_lds(num_experts) <= kLdsBytes) t = GemmTile{3, 16, 4, 2, 0, 4};
+    if (ok && nv == 2 && v[0] == 48 && v[1] == 512 && !regs) {
+      if (k % 512 == 0 && mid_lds(num_experts) <= kLdsBytes) t = GemmTile{3, 32, 8, 2, 0, 4};
       return t;
     }
     if (ok && nv == 2 && v[0] == 256 && v[1] == 256 && !regs) {
@@ -157,13 +157,13 @@ void log_tile(const char* entry, int32_t num_experts, int64_t m_total, int64_t n
   static std::mutex mu;
   static std::string last;
   char line[320];
-  const char* kind = t.tiled == 7 ? "256x256 workgroup tile for experts of >= 96 rows, 48x256 "
+  const char* kind = t.tiled == 7 ? "256x256 workgroup tile for experts of >= 96 rows, 48x512 "
                                     "workgroup items for 17-95 rows, 16x64 per-wave items below"
-                     : t.tiled == 6 ? "48x256 workgroup items for experts of >= 17 rows, 16x64 "
+                     : t.tiled == 6 ? "48x512 workgroup items for experts of >= 17 rows, 16x64 "
                                       "per-wave items below"
-                     : t.tiled == 5 ? "256x256 workgroup tile for experts of >= 96 rows, 48x256 "
+                     : t.tiled == 5 ? "256x256 workgroup tile for experts of >= 96 rows, 48x512 "
                                       "workgroup items for the rest"
-                     : t.tiled == 4 ? "48x256 workgroup items for every expert"
+                     : t.tiled == 4 ? "48x512 workgroup items for every expert"
                      : t.tiled == 3 ? (t.f8 ? "256x256 workgroup tile (FP8 split-K) for every expert"
                                            : "256x256 workgroup tile for every expert")
                      : t.tiled == 2 ? (t.f8 ? "256x256 workgroup tile (FP8 split-K) for experts of "
@@ -247,7 +247,7 @@ hipError_t launch_grouped_gemm(const GemmArgs& p, const GemmTile& t, hipStream_t
   if (t.tiled == 4) return launch_grouped_gemm_mid(p, stream);
   if (t.tiled >= 5) {
     // Launches over disjoint expert-size ranges: the large tile from kBigRows
-    // rows (5, 7), 48 x 256 items in between, per-wave items below kMidRows (6, 7).
+    // rows (5, 7), 48 x 512 items in between, per-wave items below kMidRows (6, 7).
     const bool use_big = t.tiled != 6, use_pw = t.tiled != 5;
     hipError_t err = hipSuccess;
     if (use_big) {
@@ -260,7 +260,6 @@ hipError_t launch_grouped_gemm(const GemmArgs& p, const GemmTile& t, hipStream_t
     GemmArgs mid = p;
     mid.rows_lo = use_pw ? kMidRows : 0;
     mid.rows_hi = use_big ? kBigRows : 0;
-    mid.n_tiles = (int32_t)((p.n + 255) / 256);
     err = launch_grouped_gemm_mid(mid, stream);
     if (err != hipSuccess || !use_pw) return err;
     GemmArgs small = p;

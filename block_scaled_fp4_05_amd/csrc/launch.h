@@ -26,9 +26,9 @@ struct GemmTile {
                    // items (grouped_gemm_tiled.hip); 2 = 256 x 256 items
                    // (grouped_gemm_big.hip) for experts of kBigRows rows or more
                    // and the per-wave kernel for the rest; 3 = 256 x 256 for all;
-                   // 4 = 48 x 256 items (grouped_gemm_mid.hip) for every expert;
+                   // 4 = 48 x 512 items (grouped_gemm_mid.hip) for every expert;
                    // 5, 6, 7 = splits by expert size over the large tile, the
-                   // 48 x 256 items and the per-wave items (launch_grouped_gemm)
+                   // 48 x 512 items and the per-wave items (launch_grouped_gemm)
   int f8 = 0;      // 256 x 256 items: split K by scale block on the FP8 MFMA
                    // instead of dequantising to FP16 (MOE_FP4_TILE "256x256f8")
 };
@@ -144,8 +144,9 @@ size_t tiled_lds(int32_t num_experts);
 hipError_t launch_grouped_gemm_big(const GemmArgs& args, bool f8, hipStream_t stream);
 size_t big_lds(int32_t num_experts);
 
-// Workgroup kernel for experts of a few dozen rows (grouped_gemm_mid.hip): 48 x 256
-// items, 4 waves of 64 columns each, activations shared in LDS; needs k % 512 == 0.
+// Workgroup kernel for experts of a few dozen rows (grouped_gemm_mid.hip): 48 x 512
+// items, 8 waves of 64 columns each, activations shared in LDS; needs k % 512 == 0.
+// Sets its own n_tiles.
 hipError_t launch_grouped_gemm_mid(const GemmArgs& args, hipStream_t stream);
 size_t mid_lds(int32_t num_experts);
 
@@ -158,7 +159,7 @@ constexpr size_t kLdsBytes = 160 * 1024;
 // 256 -> 352, 384 -> 359.
 constexpr int32_t kBigRows = 96;
 
-// Rows from which an expert takes the 48 x 256 items when per-wave items take
+// Rows from which an expert takes the 48 x 512 items when per-wave items take
 // the smaller experts (GemmTile.tiled 6 and 7): one 16-row block gains nothing
 // from sharing the weight conversion.
 constexpr int32_t kMidRows = 17;

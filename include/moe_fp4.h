@@ -394,10 +394,10 @@ typedef struct {
  * registers); workgroup items "128x128", "256x256" (experts of 96 rows or more;
  * per-wave items for the rest), "256x256!" (every expert), "256x256f8" and
  * "256x256f8!" (the same with K split by scale block on the FP8 MFMA),
- * "48x256" (every expert), and the splits by expert size "256x256m" (256 x 256
- * from 96 rows, 48 x 256 below: the default when experts average 96 rows or
- * more and K is a multiple of 512), "48x256p" (48 x 256 from 17 rows, per-wave
- * items below) and "256x256mp" (all three).  The 48 x 256 items need K to be a
+ * "48x512" (every expert), and the splits by expert size "256x256m" (256 x 256
+ * from 96 rows, 48 x 512 below: the default when experts average 96 rows or
+ * more and K is a multiple of 512), "48x512p" (48 x 512 from 17 rows, per-wave
+ * items below) and "256x256mp" (all three).  The 48 x 512 items need K to be a
  * multiple of 512; asked for otherwise, the default choice stands.
  */
 int moe_grouped_gemm_fp4_plan(int32_t num_experts, int64_t m_total, int64_t n, int64_t k,

@@ -118,15 +118,15 @@ def test_plan_picks_tiles_by_rows_per_expert(monkeypatch):
     assert m.plan(8192, 512 * 8192, 512, 6144)["tile_m"] == 128
     monkeypatch.setenv("MOE_FP4_TILE", "48x64")  # unsupported -> ignored
     assert m.plan(256, 4096, 512, 6144)["tile_m"] == 16
-    monkeypatch.setenv("MOE_FP4_TILE", "48x256")
+    monkeypatch.setenv("MOE_FP4_TILE", "48x512")
     p = m.plan(256, 4096, 512, 6144)
-    assert (p["tile_m"], p["tile_n"], p["k_step"], p["waves_per_group"]) == (48, 256, 256, 4)
-    assert p["lds_bytes"] == 2064 + 2 * 48 * 528 + 16
+    assert (p["tile_m"], p["tile_n"], p["k_step"], p["waves_per_group"]) == (48, 512, 256, 8)
+    assert p["lds_bytes"] == 2064 + 2 * 48 * 528 + 8 * (2 * 4096 + 1024) + 16
     assert m.plan(256, 4096, 512, 6400)["tile_m"] == 16  # K not a multiple of 512 -> default
     for split in ("256x256m", "256x256mp"):
         monkeypatch.setenv("MOE_FP4_TILE", split)
         assert m.plan(256, 4096, 512, 6144)["tile_m"] == 256
-    monkeypatch.setenv("MOE_FP4_TILE", "48x256p")
+    monkeypatch.setenv("MOE_FP4_TILE", "48x512p")
     assert m.plan(256, 4096, 512, 6144)["k_step"] == 256
 
 

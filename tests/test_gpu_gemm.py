@@ -282,8 +282,8 @@ WG_CASES = [(2, [300, 520], 320, 1024), (3, [257, 0, 40], 272, 512), (1, [600], 
             (5, [95, 96, 97, 0, 1], 192, 512)]
 
 
-@pytest.mark.parametrize("tile", ["128x128", "256x256", "256x256!", "256x256f8", "256x256f8!", "48x256",
-                                  "256x256m", "48x256p", "256x256mp"])
+@pytest.mark.parametrize("tile", ["128x128", "256x256", "256x256!", "256x256f8", "256x256f8!", "48x512",
+                                  "256x256m", "48x512p", "256x256mp"])
 @pytest.mark.parametrize("case", range(len(WG_CASES)))
 def test_workgroup_tiles_several_tiles_per_expert(case, tile):
     E, rows, n, k = WG_CASES[case]
@@ -296,14 +296,17 @@ def test_workgroup_tiles_several_tiles_per_expert(case, tile):
     assert np.array_equal(got, ref)
 
 
-# (E, rows per expert, n, k) for the 48 x 256 workgroup items: every count of live
+# (E, rows per expert, n, k) for the 48 x 512 workgroup items: every count of live
 # 16-row blocks (1-3), experts of more than 48 rows (several M-chunks, a ragged
-# last one), n not a multiple of 256 (a partial wave group of 16 or 32 rows and
-# waves wholly past n), empty experts, K of 1 to 12 granules.
+# last one), n not a multiple of 512 (a wave's 64-row group partly or wholly past
+# n) and n over 512 (three N-chunks, the last holding 16 rows), empty experts, K
+# of 1 to 12 granules (an odd count leaves the last 1024-element scale span half
+# used).
 MID_CASES = [(6, [1, 17, 33, 49, 64, 0], 256, 512),
              (4, [65, 130, 16, 31], 336, 1024),
              (3, [48, 0, 200], 80, 1536),
-             (2, [95, 96], 512, 6144)]
+             (2, [95, 96], 512, 6144),
+             (3, [20, 50, 7], 1040, 2560)]
 
 
 @pytest.mark.parametrize("case", range(len(MID_CASES)))
@@ -311,10 +314,10 @@ def test_mid_tile_every_live_row_block_count(case):
     E, rows, n, k = MID_CASES[case]
     P = _random_problem(E, rows, n, k, 780 + case, a_rows=sum(rows) + 7)
     idx = np.random.default_rng(781 + case).integers(0, sum(rows) + 7, P["m_total"]).astype(np.int32)
-    say(f"gemm tile=48x256 E={E} rows={rows} n={n} k={k}")
-    ref = _gpu_gemm(P, a_row_index=idx, extra_rows=2, tile="48x256")
-    _check_rows(ref, P, a_row_index=idx, label=f"48x256 case {case}")
-    got = _gpu_gemm(P, a_row_index=idx, extra_rows=2, tile="48x256", packed=True)
+    say(f"gemm tile=48x512 E={E} rows={rows} n={n} k={k}")
+    ref = _gpu_gemm(P, a_row_index=idx, extra_rows=2, tile="48x512")
+    _check_rows(ref, P, a_row_index=idx, label=f"48x512 case {case}")
+    got = _gpu_gemm(P, a_row_index=idx, extra_rows=2, tile="48x512", packed=True)
     assert np.array_equal(got, ref)
     # Same K order as the per-wave kernel on packed weights: equal up to the
     # MFMA's accumulation order only where a row block's sums are split
@@ -323,8 +326,8 @@ def test_mid_tile_every_live_row_block_count(case):
     _check_rows(plain, P, a_row_index=idx, label=f"default tile case {case}")
 
 
-@pytest.mark.parametrize("name,tile", [("c5", "48x256"), ("c5b", "48x256"), ("c3", "48x256"),
-                                       ("c5", "256x256m"), ("c5", "256x256mp"), ("c5b", "48x256p")])
+@pytest.mark.parametrize("name,tile", [("c5", "48x512"), ("c5b", "48x512"), ("c3", "48x512"),
+                                       ("c5", "256x256m"), ("c5", "256x256mp"), ("c5b", "48x512p")])
 def test_mid_tile_full_size_sampled_rows(name, tile):
     P, idx = _workload_problem(name)
     say(f"gemm workload {name} tile={tile} (sampled rows)")
