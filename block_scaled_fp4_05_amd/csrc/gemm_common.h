@@ -17,6 +17,16 @@ constexpr int kXcds = 8;
 constexpr int kRawBufferWord3 = 0x00020000;
 // A buffer offset past every resource built here (each covers < 2^31 bytes).
 constexpr uint32_t kOutOfRange = 0x80000000u;
+// Cache-policy operand of a buffer load on gfx950: bit 1 is the non-temporal
+// hint, which lets the caches drop the line first.  The decode and 48-row
+// kernels load their weight codes with it: a weight tile streams through once
+// (or twice, close together), and without the hint those streams push the
+// activation rows, which every N-tile of an expert reads again, out of the
+// caches.  Measured on the decode gate+up shard (256 experts x 16 rows, K 6144,
+// N 512): 86.4 -> 77.5 us; on the down projection 66 -> 61.5 us; on the Zipf
+// experts below 96 rows 278 -> 271 us for the whole GEMM.  The hint on the
+// activation loads made the decode shard slower (91.4 us).
+constexpr int kLoadStreamOnce = 2;
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 // Pointers the compiler reads through the scalar cache (uniform addresses).

@@ -309,8 +309,10 @@ __device__ __forceinline__ void issue_loads(Stage<MB, NBW, KSUB>& st, const Item
     for (int jb = 0; jb < NBW; ++jb) {
 #pragma unroll
       for (int s = 0; s < KSUB; ++s) {
-        st.w[jb][s][0] = __builtin_amdgcn_raw_buffer_load_b128(it.w, it.w_voff[jb] + kS * s, qw, 0);
-        st.w[jb][s][1] = __builtin_amdgcn_raw_buffer_load_b128(it.w, it.w_voff[jb] + kS * s + kH, qw, 0);
+        st.w[jb][s][0] =
+            __builtin_amdgcn_raw_buffer_load_b128(it.w, it.w_voff[jb] + kS * s, qw, kLoadStreamOnce);
+        st.w[jb][s][1] = __builtin_amdgcn_raw_buffer_load_b128(it.w, it.w_voff[jb] + kS * s + kH,
+                                                               qw, kLoadStreamOnce);
       }
       if constexpr (!SL) load_scales<KSUB>(st.ws[jb], it.ws, it.ws_voff[jb], sk);
     }

@@ -140,8 +140,9 @@ __device__ __forceinline__ void mid_issue(MidStage& s, const MidLoads& l, const 
   constexpr uint32_t kHalf = PK ? 1024u : 16u;
 #pragma unroll
   for (int jb = 0; jb < 4; ++jb) {
-    s.w[jb][0] = __builtin_amdgcn_raw_buffer_load_b128(l.w, l.wq[jb] | kill, qw, 0);
-    s.w[jb][1] = __builtin_amdgcn_raw_buffer_load_b128(l.w, (l.wq[jb] + kHalf) | kill, qw, 0);
+    s.w[jb][0] = __builtin_amdgcn_raw_buffer_load_b128(l.w, l.wq[jb] | kill, qw, kLoadStreamOnce);
+    s.w[jb][1] =
+        __builtin_amdgcn_raw_buffer_load_b128(l.w, (l.wq[jb] + kHalf) | kill, qw, kLoadStreamOnce);
   }
 }
 
