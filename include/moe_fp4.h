@@ -256,7 +256,7 @@ int moe_grouped_gemm_fp4_packed(const uint8_t* a_q, const uint8_t* a_sf, const f
  * Device-wide FP32 atomic adds complete at about 3.2e11 per second however
  * the destinations are spread over the XCDs, so the top-k adds alone take
  * longer than the whole two-pass finalize (down-projection shard: 50 million
- * adds, at least 156 us, against 83 us for GEMM and combine).
+ * adds, at least 156 us, against 80 us for GEMM and combine).
  * Errors: as moe_grouped_gemm_fp4, plus NULL (out_token, row_weight), SHAPE
  * (num_tokens < 1), ALIGN (out_token, row_weight, out not 4-byte aligned), ARG
  * (w_packed not 0 or 1), UNSUPPORTED (num_tokens * ldo * 4 >= 2^31 - 4096, or a
