@@ -26,7 +26,8 @@ the same thing).
   python bench.py --finalize   # + finalize: fused atomics vs plain GEMM + token-order combine
   python bench.py --layer      # + a whole MoE FFN layer (eager and from a HIP graph)
   python bench.py --copy-calibration   # a plain copy of known size, for counter scaling
-  python bench.py --ceilings           # torch's read / write / copy rates on 1 GiB
+  python bench.py --ceilings           # torch's read / write / copy rates on 1 GiB, and the
+                                       # decode weight-stream pattern with no arithmetic
 """
 from __future__ import annotations
 
@@ -78,7 +79,7 @@ def parse_args():
                          "with the SwiGLU + NVFP4 epilogue, down-projection GEMM, token-order "
                          "combine (the workload's weights are the gate+up projection)")
     ap.add_argument("--ceilings", action="store_true",
-                    help="only print torch's read, write and copy rates on 1 GiB (streaming context)")
+                    help="only print streaming rates: torch's read, write and copy on 1 GiB and the decode weight-stream pattern with no arithmetic")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a device copy of known size (counter scale factor)")
     return ap.parse_args()
@@ -767,8 +768,58 @@ def ceilings():
     out["read_1GiB_sum"] = rate(lambda: a.sum(), nbytes)
     out["write_1GiB_fill"] = rate(lambda: b.fill_(2.0), nbytes)
     out["copy_1GiB"] = rate(lambda: b.copy_(a), 2 * nbytes)
+    del a, b
+    out["stream_probe"] = stream_probe_rates()
     out["peak_gbps"] = HBM_PEAK_GBS
     print(json.dumps({"ceilings": out}), flush=True)
+
+
+def stream_probe_rates():
+    """Read rates of the decode GEMM's weight-stream pattern with no arithmetic
+    (libmoe_fp4_probe.so, built by build()): 2,048 wavefronts, each reading one
+    decode N-tile's weights (64 rows x 6,144 K x 0.5625 bytes = 221,184 bytes) in
+    16 KB stages of 1 KB loads, two stages in flight; in its own region per
+    wavefront (the GEMM's layout) or with the wavefronts sweeping the buffer
+    together; with and without the non-temporal hint.  Three copies of the
+    buffer (1.36 GB, more than the caches hold) are read in turn."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "block_scaled_fp4_05_amd", "libmoe_fp4_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: run __graft_entry__.build() first")
+    L = ctypes.CDLL(path)
+    fn = L.moe_fp4_stream_probe
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    waves, per_wave = 2048, 64 * 6144 * 9 // 16
+    stages = per_wave // 16384
+    nbytes = waves * per_wave
+    read = waves * stages * 16384
+    g = torch.Generator(device="cuda").manual_seed(5)
+    bufs = [torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda", generator=g)
+            for _ in range(3)]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = {"waves": waves, "bytes_read_per_launch": read}
+    for layout, lname in ((0, "regions"), (1, "interleaved")):
+        for nt in (0, 1):
+            def run(i):
+                rc = fn(bufs[i % 3].data_ptr(), nbytes, per_wave, stages, waves, layout, nt,
+                        sink.data_ptr(), stream)
+                if rc != 0:
+                    raise RuntimeError(f"moe_fp4_stream_probe returned {rc}")
+            warm(run)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(30):
+                run(i)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / 30 * 1e3
+            res[f"{lname}_{'nt' if nt else 'plain'}"] = {
+                "us": round(us, 1), "gbps": round(read / (us * 1e-6) / 1e9, 1)}
+    return res
 
 
 def copy_calibration():

@@ -12,6 +12,10 @@ LIB = os.path.join(PKG, "libmoe_fp4.so")
 SOURCES = ["api.cpp", "quantize.hip", "grouped_gemm.hip", "grouped_gemm_finalize.hip",
            "grouped_gemm_swiglu.hip", "grouped_gemm_tiled.hip", "grouped_gemm_big.hip", "grouped_gemm_mid.hip", "pack.hip", "combine.hip"]
 HEADERS = ["fp4_device.h", "gemm_common.h", "grouped_gemm_kernel.h", "launch.h"]
+# A measurement aid kept out of the library: the streaming-read probe that
+# bench.py --ceilings loads (not part of the C ABI in include/moe_fp4.h).
+PROBE_LIB = os.path.join(PKG, "libmoe_fp4_probe.so")
+PROBE_SOURCES = ["stream_probe.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -30,12 +34,14 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False, out: str | None = None, extra_flags=()) -> str:
+def build(verbose: bool = False, out: str | None = None, extra_flags=(), sources=None) -> str:
     """Always recompiles (each source to an object in parallel, then one link);
     writes the library atomically to `out` (default: the in-tree library).
     `extra_flags` go on every compile and the link (the host-sanitizer build of
-    the CPU tests passes -Xarch_host flags here)."""
+    the CPU tests passes -Xarch_host flags here).  `sources` defaults to the
+    library's; build_probe() passes the probe's."""
     out = out or LIB
+    srcs = list(sources or SOURCES)
     from concurrent.futures import ThreadPoolExecutor
     import tempfile
 
@@ -48,11 +54,11 @@ def build(verbose: bool = False, out: str | None = None, extra_flags=()) -> str:
                    os.path.join(CSRC, src), "-o", obj]
             return obj, subprocess.run(cmd, capture_output=True, text=True)
 
-        workers = max(1, min(len(SOURCES), os.cpu_count() or 1, 8))
+        workers = max(1, min(len(srcs), os.cpu_count() or 1, 8))
         with ThreadPoolExecutor(max_workers=workers) as pool:
-            results = list(pool.map(compile_one, SOURCES))
+            results = list(pool.map(compile_one, srcs))
         log = []
-        for (obj, res), src in zip(results, SOURCES):
+        for (obj, res), src in zip(results, srcs):
             log.append(res.stdout + res.stderr)
             if res.returncode != 0:
                 raise RuntimeError(f"hipcc failed on {src}:\n" + res.stdout + res.stderr)
@@ -68,5 +74,11 @@ def build(verbose: bool = False, out: str | None = None, extra_flags=()) -> str:
     return out
 
 
+def build_probe(verbose: bool = False) -> str:
+    """The streaming-read probe library (libmoe_fp4_probe.so)."""
+    return build(verbose=verbose, out=PROBE_LIB, sources=PROBE_SOURCES)
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_probe(verbose=True))
