@@ -112,7 +112,11 @@ struct MidLoads {
 // the wave's sink), then the activations (the end of the previous stage waits
 // for them), then the weight codes.  Past the last stage (`past`) every offset
 // is pushed out of range, so the loads return zeros without memory traffic and
-// every issue stays unconditional.
+// every issue stays unconditional.  The activation offsets, scalar part
+// included, stay far below 2^32 even then (rows of at most 2^31 - 4097 bytes
+// in all, a few hundred bytes past a row's end), so a past stage's activations
+// are zero, and its products add exact zeros whatever its weight loads return
+// (a dequantised weight is always finite).
 template <bool PK, int SUB>
 __device__ __forceinline__ void mid_issue(MidStage& s, const MidLoads& l, const rsrc_t& a_rs,
                                           const rsrc_t& as_rs, int32_t st, bool past,

@@ -96,6 +96,16 @@ def test_log_prints_the_chosen_tile_and_the_output_range_fallback(monkeypatch, c
     assert capfd.readouterr().err == ""
 
 
+def test_log_keeps_the_48_row_items_at_the_largest_ldo(monkeypatch, capfd):
+    """48 rows of 2^23 BF16 values stay below 2^31 - 4096 bytes, so the 48 x 512 items
+    run at every accepted ldo (test_gpu_limits checks their output there); with K not a
+    multiple of 512 the request falls back to the default choice."""
+    err = _log_of_empty_call(monkeypatch, capfd, "48x512", 2 ** 23, E=3, n=272, k=512)
+    assert "48x512 workgroup items for every expert" in err, err
+    err = _log_of_empty_call(monkeypatch, capfd, "48x512", 2 ** 23, E=3, n=272, k=256)
+    assert "48x512" not in err, err
+
+
 def test_plan_picks_tiles_by_rows_per_expert(monkeypatch):
     m = _lib()
     monkeypatch.delenv("MOE_FP4_TILE", raising=False)

@@ -112,8 +112,20 @@ def test_workgroup_tiles_at_the_largest_ldo(tile, ldo):
     falls back to per-wave items; just below that bound the workgroup tile itself
     runs.  Every row is checked, the padding columns and the rows past m_total keep
     their canary."""
-    E, n, k = 3, 272, 256
-    off = np.array([0, 300, 300, 317], np.int32)
+    _workgroup_tile_case(tile, ldo, 256, np.array([0, 300, 300, 317], np.int32))
+
+
+@pytest.mark.parametrize("ldo", [2 ** 23, 2 ** 23 - 24])
+def test_mid_tile_at_the_largest_ldo(ldo):
+    """48-row workgroup items at the largest accepted ldo: 48 rows of 2^23 BF16 values
+    stay below 2^31 bytes, so the 48 x 512 kernel itself runs (K = 512, its smallest);
+    a 100-row expert (items of 48, 48 and 4 rows), an empty one and a 17-row one, n = 272
+    (a partial 512-column item), every row checked, canaries kept."""
+    _workgroup_tile_case("48x512", ldo, 512, np.array([0, 100, 100, 117], np.int32))
+
+
+def _workgroup_tile_case(tile, ldo, k, off):
+    E, n = 3, 272
     m = int(off[-1])
     extra = 8
     a_q = gen.random_fp4_bytes((m, k // 2), 61)
@@ -185,7 +197,7 @@ def test_byte_offsets_at_the_32_bit_limit():
                               w1_sf[cols][None], w_scale[1:], np.array([0, m], np.int32))
     del a_q_h, a_sf_h
     args = (a_q, a_sf, dev(np.array([a_scale])), w_q, w_sf, dev(w_scale), dev(off), m)
-    for tile in [None, "16x64", "64x64", "128x128", "256x256!"]:
+    for tile in [None, "16x64", "64x64", "128x128", "256x256!", "48x512"]:
         say(f"limits: byte offsets, tile={tile}")
         out = _gemm(*args, row_index=dev(picks), tile=tile)
         _check(bf16_bits_of(out)[:, cols], R, ref, f"32-bit byte offsets, tile {tile}")
@@ -195,6 +207,10 @@ def test_byte_offsets_at_the_32_bit_limit():
     out = _gemm(a_q, a_sf, args[2], packed, w_sf, args[5], args[6], m, row_index=dev(picks),
                 packed=True)
     _check(bf16_bits_of(out)[:, cols], R, ref, "32-bit byte offsets, packed")
+    say("limits: byte offsets, packed weights, 48x512 workgroup items")
+    out = _gemm(a_q, a_sf, args[2], packed, w_sf, args[5], args[6], m, row_index=dev(picks),
+                tile="48x512", packed=True)
+    _check(bf16_bits_of(out)[:, cols], R, ref, "32-bit byte offsets, packed, 48x512")
 
 
 def test_combine_buffers_at_the_32_bit_limit():
